@@ -1,0 +1,368 @@
+"""fp64 definitions of the Stem prefill path: OAM scoring, TPD budget, top-k
+block selection and causal block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Not imported by the
+product path.
+
+Sources (web pages; no code exists on them):
+  [Stem-cn]  "腾讯混元Stem稀疏注意力算法：长文推理加速新SOTA" (cn486.com) —
+             §一.3.1 Token Position Decay, §一.3.2 Output-Aware Metric,
+             §二.1 challenges of existing operators, §二.2.1 Stem operator,
+             §二.2.2 BSA operator, §二.3 operator benchmark.
+  [Stem-en]  "Tencent Hunyuan introduces Stem sparse attention algorithm"
+             (setupai.cc) — "Technical Deep Dive".
+
+Conventions (shared with the library's documented interface, not its code):
+  q  [batch, S, Hq, d]     token-major, head-interleaved (as a KV cache stores it)
+  k,v[batch, S, Hkv, d]    Hq % Hkv == 0, query head h reads KV head h // (Hq/Hkv)
+  blocks of B tokens, Nb = S / B; I indexes query blocks, J key blocks.
+
+Readings taken where the pages are silent (each is the plainest one the rest
+of the text supports; "parity unpinned against the authors" for the OAM form,
+the pooling, the norm type and the TPD shape):
+  * OAM (Stem-cn §一.3.2: contribution = routing probability x value
+    magnitude; §二.2.1: the metric is purely additive, needs no softmax):
+    log(p_ij * |v_j|) = tau*q.k - LSE_i + ln|v_j|; the LSE is constant per
+    query row, so rows are ranked by tau*q.k + ln|v|.  At block level the
+    compact representation is the mean of the block's rows (the mean of all
+    B x B pairwise logits equals the logit of the means, by bilinearity) and
+    the value magnitude is the Frobenius norm of the block's V rows.
+  * TPD (Stem-cn §一.3.1; Stem-en Deep Dive): a fixed total of kept blocks,
+    redistributed towards early query blocks by water-filling; see
+    ``tpd_budget``.
+  * Selection: the sink block J=0 and the diagonal J=I are always kept; the
+    rest of the row's budget goes to the highest-scoring J in [1, I-1], equal
+    scores to the smaller J, NaN below everything.
+"""
+
+from __future__ import annotations
+
+import heapq
+import math
+from fractions import Fraction
+
+import numpy as np
+
+E4M3_MAX = 448.0  # largest finite OCP FP8 E4M3 ("e4m3fn") value: 1.75 * 2**8
+
+
+# --------------------------------------------------------------------------
+# Inputs
+# --------------------------------------------------------------------------
+
+def e4m3fn_round(x):
+    """Round to the nearest OCP FP8 E4M3 value (ties to even), saturating at
+    +-448.  Written from the format definition: 1 sign bit, 4 exponent bits
+    with bias 7, 3 mantissa bits, no infinities; normal numbers from 2**-6,
+    subnormals are multiples of 2**-9.  The pages name FP8 quantisation
+    (Stem-cn §二.2.2) without a rounding rule; this is the OCP default.
+    Returns fp64 values (exactly representable in E4M3)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)                      # a = m * 2**e with m in [0.5, 1)
+    exp = np.maximum(e - 1, -6)             # binade exponent, floored at the normal minimum
+    quantum = np.ldexp(1.0, exp - 3)        # spacing of 3-bit mantissas in that binade
+    r = np.round(a / quantum) * quantum     # np.round: round half to even
+    r = np.minimum(r, E4M3_MAX)
+    r = np.where(a == 0, 0.0, r)
+    return np.copysign(r, x)
+
+
+def dequantize(values, scale=1.0):
+    """x = x_q * scale in fp64 (per-tensor scale; 1 for unquantised inputs)."""
+    return np.asarray(values, dtype=np.float64) * float(scale)
+
+
+# --------------------------------------------------------------------------
+# OAM scoring  [Stem-cn §一.3.2, §二.2.1]
+# --------------------------------------------------------------------------
+
+def pool_blocks(q, k, v, block):
+    """Compact per-block representations (Stem-cn §二.2.1: Q and K are first
+    reduced to block-level representations, then one GEMM scores all blocks).
+
+    Returns
+      qbar [b, Hq, Nb, d]   mean of the block's query rows
+      kbar [b, Hkv, Nb, d]  mean of the block's key rows
+      lvn  [b, Hkv, Nb]     ln of the Frobenius norm of the block's value rows
+                            (the "value magnitude" of Stem-cn §一.3.2)
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    nb = S // block
+    qbar = q.reshape(b, nb, block, Hq, d).mean(axis=2).transpose(0, 2, 1, 3)
+    kbar = k.reshape(b, nb, block, Hkv, d).mean(axis=2).transpose(0, 2, 1, 3)
+    sq = (v.reshape(b, nb, block, Hkv, d) ** 2).sum(axis=(2, 4))      # [b, Nb, Hkv]
+    with np.errstate(divide="ignore"):
+        lvn = 0.5 * np.log(sq).transpose(0, 2, 1)
+    return qbar, kbar, lvn
+
+
+def oam_scores(q, k, v, block, softmax_scale=None):
+    """Block scores s[b, h, I, J] = tau * <qbar_hI, kbar_gJ> + lvn_gJ for J <= I,
+    -inf above the diagonal (no causal block there).  tau is the attention
+    softmax scale (1/sqrt(d) unless given), g = h // (Hq/Hkv)."""
+    qbar, kbar, lvn = pool_blocks(q, k, v, block)
+    b, Hq, nb, d = qbar.shape
+    Hkv = kbar.shape[1]
+    group = Hq // Hkv
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    s = np.full((b, Hq, nb, nb), -np.inf)
+    upper = np.triu(np.ones((nb, nb), dtype=bool), 1)
+    for bi in range(b):
+        for h in range(Hq):
+            g = h // group
+            row = tau * (qbar[bi, h] @ kbar[bi, g].T) + lvn[bi, g][None, :]
+            row[upper] = -np.inf
+            s[bi, h] = row
+    return s
+
+
+# --------------------------------------------------------------------------
+# TPD budget  [Stem-cn §一.3.1; Stem-en Technical Deep Dive]
+# --------------------------------------------------------------------------
+
+def causal_block_count(nb):
+    """Blocks on or below the diagonal: Nb (Nb + 1) / 2."""
+    return nb * (nb + 1) // 2
+
+
+def tpd_total(nb, density):
+    """Total kept blocks per head: T = floor(density * C + 1/2) in fp64, with
+    C the causal block count, clamped to [2 Nb - 1, C] (the forced sink and
+    diagonal blocks always count; Stem-cn §一.3.1 fixes the total, TPD only
+    moves it)."""
+    if not (0.0 < density <= 1.0):
+        raise ValueError("density must lie in (0, 1]")
+    c = causal_block_count(nb)
+    t = int(math.floor(density * c + 0.5))
+    return max(2 * nb - 1, min(c, t))
+
+
+def _tpd_key(alpha, i, n):
+    """Water-filling key of granting row i its n-th block: n / (i+1)**(1-alpha).
+    Compared exactly: for alpha = 0 the key is n/(i+1), for alpha = 1/2 its
+    square n**2/(i+1) (same order), for alpha = 1 it is n."""
+    if alpha == 0.0:
+        return Fraction(n, i + 1)
+    if alpha == 0.5:
+        return Fraction(n * n, i + 1)
+    if alpha == 1.0:
+        return Fraction(n)
+    raise ValueError("alpha must be 0, 0.5 or 1")
+
+
+def tpd_budget(nb, density, alpha=0.5):
+    """Per-query-block budget k[I] (kept KV blocks in row I) and the total T.
+
+    The pages: a position-dependent top-k inside each layer that gives early
+    positions a larger share, at the same total as a uniform budget
+    (Stem-cn §一.3.1; Stem-en Deep Dive).  Reading: start every row at its
+    forced minimum (k[0] = 1: sink and diagonal coincide; k[I] = 2 otherwise),
+    then hand out the remaining T - sum(k) blocks one at a time, each to the
+    row with the smallest key (k[I]+1) / (I+1)**(1-alpha) that still has room
+    (k[I] < I+1), equal keys to the smaller I.  The keep ratio then decays as
+    (I+1)**-alpha; alpha = 0 is the uniform ratio, alpha = 1 a uniform count.
+    """
+    t = tpd_total(nb, density)
+    k = [1] + [2] * (nb - 1)
+    if nb == 1:
+        return [1], t
+    heap = []
+    for i in range(nb):
+        if k[i] < i + 1:
+            heap.append((_tpd_key(alpha, i, k[i] + 1), i))
+    heapq.heapify(heap)
+    remaining = t - sum(k)
+    while remaining > 0:
+        _, i = heapq.heappop(heap)
+        k[i] += 1
+        remaining -= 1
+        if k[i] < i + 1:
+            heapq.heappush(heap, (_tpd_key(alpha, i, k[i] + 1), i))
+    return k, t
+
+
+# --------------------------------------------------------------------------
+# Top-k selection  [Stem-cn §一.3.1-§一.3.2, §二.2.1]
+# --------------------------------------------------------------------------
+
+def select_row(scores_row, i, budget):
+    """Kept key blocks of query block i: {0, i} plus the best (budget - |{0,i}|)
+    of J in [1, i-1] ranked by score descending, ties to the smaller J, NaN
+    last.  Returns a sorted list of J."""
+    forced = {0, i}
+    need = budget - len(forced)
+    cand = np.arange(1, i)
+    if need > 0 and cand.size:
+        vals = np.asarray(scores_row, dtype=np.float64)[cand]
+        nan = np.isnan(vals)
+        # primary: NaN last; secondary: score descending; tertiary: J ascending
+        order = np.lexsort((cand, -np.where(nan, 0.0, vals), nan))
+        forced.update(int(j) for j in cand[order[:need]])
+    return sorted(forced)
+
+
+def select_blocks(scores, budget):
+    """Boolean block mask [b, Hq, Nb, Nb] from block scores and per-row budget."""
+    scores = np.asarray(scores, dtype=np.float64)
+    b, hq, nb, _ = scores.shape
+    mask = np.zeros((b, hq, nb, nb), dtype=bool)
+    for bi in range(b):
+        for h in range(hq):
+            for i in range(nb):
+                mask[bi, h, i, select_row(scores[bi, h, i], i, budget[i])] = True
+    return mask
+
+
+def pack_block_mask(mask):
+    """Bit J of 32-bit word J // 32 in row (b, h, I) is set when block J is
+    kept; words [b, Hq, Nb, ceil(Nb/32)] little-endian bit order."""
+    mask = np.asarray(mask, dtype=bool)
+    b, hq, nb, _ = mask.shape
+    words = (nb + 31) // 32
+    out = np.zeros((b, hq, nb, words), dtype=np.uint32)
+    for j in range(nb):
+        out[..., j // 32] |= mask[..., j].astype(np.uint32) << np.uint32(j % 32)
+    return out
+
+
+def unpack_block_mask(words, nb):
+    words = np.asarray(words, dtype=np.uint32)
+    j = np.arange(nb)
+    return ((words[..., j // 32] >> (j % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+# --------------------------------------------------------------------------
+# Block-sparse attention  [Stem-cn §二.2.2]
+# --------------------------------------------------------------------------
+
+def _visible_keys(block_mask_row, i_blk, block):
+    """Token indices of the kept blocks J <= I (bits above the diagonal are
+    ignored: the attention is causal)."""
+    js = [j for j in range(i_blk + 1) if block_mask_row[j]]
+    if not js:
+        return np.zeros(0, dtype=np.int64), False
+    idx = np.concatenate([np.arange(j * block, (j + 1) * block) for j in js])
+    return idx, (i_blk in js)
+
+
+def _attend(qrows, pos, keys_idx, diag_kept, i_blk, block, k_h, v_h, tau):
+    """Softmax attention of query rows at positions `pos` over the key tokens
+    `keys_idx`; inside the diagonal block a key j is visible only if j <= i.
+    A skipped key block contributes nothing, exactly as a -inf logit would
+    (Stem-cn §二.2.2).  Rows with no visible key give O = 0, LSE = -inf."""
+    d = qrows.shape[-1]
+    if keys_idx.size == 0:
+        return np.zeros((len(pos), d)), np.full(len(pos), -np.inf)
+    logits = tau * (qrows @ k_h[keys_idx].T)                     # [rows, keys]
+    if diag_kept:
+        diag_start = i_blk * block
+        in_diag = keys_idx >= diag_start
+        future = in_diag[None, :] & (keys_idx[None, :] > pos[:, None])
+        logits = np.where(future, -np.inf, logits)
+    m = logits.max(axis=1)
+    p = np.exp(logits - m[:, None])
+    l_sum = p.sum(axis=1)
+    o = (p @ v_h[keys_idx]) / l_sum[:, None]
+    return o, m + np.log(l_sum)
+
+
+def block_sparse_attention(q, k, v, block_mask, block, softmax_scale=None):
+    """O[b, S, Hq, d] and LSE[b, Hq, S] (natural log) of causal attention that
+    only sees the kept key blocks of each query block (block_mask [b,Hq,Nb,Nb]
+    bool)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    group = Hq // Hkv
+    nb = S // block
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = np.zeros((b, S, Hq, d))
+    lse = np.full((b, Hq, S), -np.inf)
+    for bi in range(b):
+        for h in range(Hq):
+            g = h // group
+            for i_blk in range(nb):
+                keys_idx, diag = _visible_keys(block_mask[bi, h, i_blk], i_blk, block)
+                pos = np.arange(i_blk * block, (i_blk + 1) * block)
+                oo, ll = _attend(q[bi, pos, h], pos, keys_idx, diag, i_blk, block,
+                                 k[bi, :, g], v[bi, :, g], tau)
+                o[bi, pos, h] = oo
+                lse[bi, h, pos] = ll
+    return o, lse
+
+
+def attention_rows(q, k, v, block_mask, block, rows, softmax_scale=None):
+    """The same definition evaluated only at the (batch, head, token) triples
+    in `rows`: for sampled checks at sizes where the full oracle is too slow.
+    block_mask is None for dense causal attention, else a callable
+    (b, h, I) -> bool row of length Nb or an array [b, Hq, Nb, Nb]."""
+    S, Hq, d = q.shape[1], q.shape[2], q.shape[3]
+    Hkv = k.shape[2]
+    group = Hq // Hkv
+    nb = S // block
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    outs, lses = [], []
+    for bi, h, i in rows:
+        i_blk = i // block
+        if block_mask is None:
+            mrow = np.ones(nb, dtype=bool)
+        elif callable(block_mask):
+            mrow = block_mask(bi, h, i_blk)
+        else:
+            mrow = block_mask[bi, h, i_blk]
+        keys_idx, diag = _visible_keys(mrow, i_blk, block)
+        g = h // group
+        qrow = np.asarray(q[bi, i, h], dtype=np.float64)[None, :]
+        kk = np.asarray(k[bi, :, g], dtype=np.float64)
+        vv = np.asarray(v[bi, :, g], dtype=np.float64)
+        oo, ll = _attend(qrow, np.array([i]), keys_idx, diag, i_blk, block, kk, vv, tau)
+        outs.append(oo[0])
+        lses.append(ll[0])
+    return np.array(outs), np.array(lses)
+
+
+def dense_causal_attention(q, k, v, softmax_scale=None):
+    """Plain causal softmax attention, row by row over all keys j <= i: the
+    dense baseline (Stem-cn §二.3) and the density-1 limit of the sparse path."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b, S, Hq, d = q.shape
+    group = Hq // k.shape[2]
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = np.zeros((b, S, Hq, d))
+    lse = np.zeros((b, Hq, S))
+    for bi in range(b):
+        for h in range(Hq):
+            g = h // group
+            for i in range(S):
+                logits = tau * (k[bi, : i + 1, g] @ q[bi, i, h])
+                m = logits.max()
+                p = np.exp(logits - m)
+                o[bi, i, h] = p @ v[bi, : i + 1, g] / p.sum()
+                lse[bi, h, i] = m + np.log(p.sum())
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# The whole path
+# --------------------------------------------------------------------------
+
+def stem_pipeline(q, k, v, block, density, alpha=0.5, softmax_scale=None):
+    """Score -> budget -> select -> block-sparse attention (Stem-cn §二.1: a
+    scoring stage that records each block's importance, then a sparse stage
+    that computes only the selected blocks).  Returns (scores, budget, mask,
+    O, LSE)."""
+    s = oam_scores(q, k, v, block, softmax_scale)
+    nb = s.shape[2]
+    budget, _ = tpd_budget(nb, density, alpha)
+    mask = select_blocks(s, budget)
+    o, lse = block_sparse_attention(q, k, v, mask, block, softmax_scale)
+    return s, budget, mask, o, lse
