@@ -1,0 +1,210 @@
+"""Python binding of the Stem block-sparse prefill-attention library (gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libstem_bsa.so`` (C ABI in ``include/stem_bsa.h``).  PyTorch supplies device
+memory and the current HIP stream.  There is no fallback: if the library is
+missing, every call raises.
+
+Entry points mirror the C names:
+  stem_score_workspace_size, stem_score, stem_tpd_budget, stem_select,
+  bsa_prefill, stem_last_error
+plus allocating conveniences ``score``, ``select`` and ``attention``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstem_bsa.so")
+
+STEM_OK, STEM_EINVAL, STEM_EUNSUPPORTED, STEM_EHIP, STEM_EWORKSPACE = 0, -1, -2, -3, -4
+STEM_F32, STEM_BF16, STEM_FP8_E4M3 = 0, 1, 2
+_DTYPES = {"f32": STEM_F32, "bf16": STEM_BF16, "fp8": STEM_FP8_E4M3}
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+
+EXPORTS = ("stem_score_workspace_size", "stem_score", "stem_tpd_budget", "stem_select",
+           "bsa_prefill", "stem_last_error")
+
+
+class StemError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"stem error {code}: {message}")
+        self.code = code
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("q_scale", ctypes.c_float),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class KvDesc(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_sparse_attention_24_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, D, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
+        h.stem_score_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
+        h.stem_score.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, SZ, P]
+        h.stem_tpd_budget.argtypes = [I32, D, D, P, ctypes.POINTER(I64)]
+        h.stem_select.argtypes = [ctypes.POINTER(AttnDesc), P, D, D, P, P, I32, P, P]
+        h.bsa_prefill.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, P, P]
+        h.stem_last_error.argtypes = []
+        h.stem_last_error.restype = ctypes.c_char_p
+        for name in EXPORTS[:-1]:
+            getattr(h, name).restype = ctypes.c_int
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(rc: int):
+    if rc != STEM_OK:
+        raise StemError(rc, lib().stem_last_error().decode())
+
+
+@dataclasses.dataclass
+class Problem:
+    """Shape and element type of one prefill problem."""
+    batch: int
+    seq_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str = "bf16"                 # "f32" | "bf16" | "fp8"
+    q_scale: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    softmax_scale: float = 0.0          # 0: 1/sqrt(head_dim)
+
+    @property
+    def num_blocks(self) -> int:
+        return self.seq_len // self.block_size
+
+    @property
+    def mask_words(self) -> int:
+        return (self.num_blocks + 31) // 32
+
+    def desc(self) -> AttnDesc:
+        return AttnDesc(self.batch, self.seq_len, self.num_q_heads, self.num_kv_heads,
+                        self.head_dim, self.block_size, _DTYPES[self.dtype], self.q_scale,
+                        self.k_scale, self.v_scale, self.softmax_scale)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _kv(k, v, block_table=None, page_size=0):
+    if block_table is None:
+        return KvDesc(k.data_ptr(), v.data_ptr(), None, 0, 0, 0)
+    return KvDesc(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), page_size,
+                  block_table.shape[1], k.shape[0])
+
+
+# ---- C entry points --------------------------------------------------------
+
+def stem_score_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    d = p.desc()
+    _check(lib().stem_score_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def stem_score(p: Problem, q, k, v, scores, workspace, block_table=None, page_size=0, stream=None):
+    d = p.desc()
+    kv = _kv(k, v, block_table, page_size)
+    _check(lib().stem_score(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(scores),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream)))
+
+
+def stem_tpd_budget(num_blocks: int, density: float, alpha: float = 0.5):
+    buf = (ctypes.c_int32 * max(num_blocks, 1))()
+    total = ctypes.c_int64(0)
+    _check(lib().stem_tpd_budget(num_blocks, density, alpha, ctypes.cast(buf, ctypes.c_void_p),
+                                 ctypes.byref(total)))
+    return [int(x) for x in buf[:num_blocks]], int(total.value)
+
+
+def stem_select(p: Problem, scores, density, alpha, mask, list_out=None, list_stride=0,
+                count=None, stream=None):
+    d = p.desc()
+    _check(lib().stem_select(ctypes.byref(d), _ptr(scores), density, alpha, _ptr(mask),
+                             _ptr(list_out), list_stride, _ptr(count), _stream(stream)))
+
+
+def bsa_prefill(p: Problem, q, k, v, mask, o, lse=None, block_table=None, page_size=0, stream=None):
+    d = p.desc()
+    kv = _kv(k, v, block_table, page_size)
+    _check(lib().bsa_prefill(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(mask), _ptr(o),
+                             _ptr(lse), _stream(stream)))
+
+
+def stem_last_error() -> str:
+    return lib().stem_last_error().decode()
+
+
+# ---- allocating conveniences -------------------------------------------------
+
+def score(p: Problem, q, k, v, block_table=None, page_size=0, stream=None):
+    """Returns (scores [b,Hq,Nb,Nb] fp32, workspace bytes as uint8)."""
+    nb = p.num_blocks
+    scores = torch.empty((p.batch, p.num_q_heads, nb, nb), dtype=torch.float32, device=q.device)
+    ws = torch.empty(stem_score_workspace_size(p), dtype=torch.uint8, device=q.device)
+    stem_score(p, q, k, v, scores, ws, block_table, page_size, stream)
+    return scores, ws
+
+
+def select(p: Problem, scores, density, alpha=0.5, with_list=False, stream=None):
+    """Returns (mask words, list or None, count or None)."""
+    nb = p.num_blocks
+    dev = scores.device
+    mask = torch.empty((p.batch, p.num_q_heads, nb, p.mask_words), dtype=torch.int32, device=dev)
+    lst = cnt = None
+    stride = 0
+    if with_list:
+        budget, _ = stem_tpd_budget(nb, density, alpha)
+        stride = max(budget)
+        lst = torch.empty((p.batch, p.num_q_heads, nb, stride), dtype=torch.int32, device=dev)
+        cnt = torch.empty((p.batch, p.num_q_heads, nb), dtype=torch.int32, device=dev)
+    stem_select(p, scores, density, alpha, mask, lst, stride, cnt, stream)
+    return mask, lst, cnt
+
+
+def attention(p: Problem, q, k, v, mask=None, block_table=None, page_size=0, with_lse=True,
+              stream=None):
+    """Returns (O [b,S,Hq,d], LSE [b,Hq,S] or None).  mask None = dense causal."""
+    odt = torch.float32 if p.dtype == "f32" else torch.bfloat16
+    o = torch.empty((p.batch, p.seq_len, p.num_q_heads, p.head_dim), dtype=odt, device=q.device)
+    lse = (torch.empty((p.batch, p.num_q_heads, p.seq_len), dtype=torch.float32, device=q.device)
+           if with_lse else None)
+    bsa_prefill(p, q, k, v, mask, o, lse, block_table, page_size, stream)
+    return o, lse

@@ -1,0 +1,209 @@
+// Host side of the C ABI declared in include/stem_bsa.h: argument checks,
+// workspace carving and kernel launches.  Nothing here allocates device
+// memory or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "stem_internal.h"
+
+using namespace stem;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return STEM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+int check_desc(const stem_attn_desc *d, Shape *s) {
+    if (!d) return fail(STEM_EINVAL, "desc is NULL");
+    if (d->batch < 1 || d->seq_len < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1)
+        return fail(STEM_EINVAL, "batch, seq_len and head counts must be positive");
+    if (d->num_q_heads % d->num_kv_heads)
+        return fail(STEM_EINVAL, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                    d->num_q_heads, d->num_kv_heads);
+    if (d->block_size != 64 && d->block_size != 128)
+        return fail(STEM_EUNSUPPORTED, "block_size %d not built (64 or 128)", d->block_size);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(STEM_EUNSUPPORTED, "head_dim %d not built (64 or 128)", d->head_dim);
+    if (d->seq_len % d->block_size)
+        return fail(STEM_EINVAL, "seq_len %d is not a multiple of block_size %d", d->seq_len,
+                    d->block_size);
+    const int nb = d->seq_len / d->block_size;
+    if (nb > 4096) return fail(STEM_EUNSUPPORTED, "more than 4096 blocks per sequence (%d)", nb);
+    if (d->dtype != STEM_F32 && d->dtype != STEM_BF16 && d->dtype != STEM_FP8_E4M3)
+        return fail(STEM_EINVAL, "unknown dtype %d", d->dtype);
+    if (!finite_pos(d->q_scale) || !finite_pos(d->k_scale) || !finite_pos(d->v_scale))
+        return fail(STEM_EINVAL, "scales must be finite and positive");
+    if (d->dtype != STEM_FP8_E4M3 && (d->q_scale != 1.0f || d->k_scale != 1.0f || d->v_scale != 1.0f))
+        return fail(STEM_EINVAL, "q/k/v scales must be 1 unless dtype is STEM_FP8_E4M3");
+    if (!std::isfinite(d->softmax_scale) || d->softmax_scale < 0.0f)
+        return fail(STEM_EINVAL, "softmax_scale must be finite and >= 0");
+    const long long elems = (long long)d->batch * d->seq_len * d->num_q_heads * d->head_dim;
+    if (elems >= (1LL << 40)) return fail(STEM_EUNSUPPORTED, "tensor too large");
+    s->batch = d->batch;
+    s->seq = d->seq_len;
+    s->hq = d->num_q_heads;
+    s->hkv = d->num_kv_heads;
+    s->d = d->head_dim;
+    s->blk = d->block_size;
+    s->nb = nb;
+    s->words = (nb + 31) / 32;
+    s->dtype = d->dtype;
+    s->q_scale = d->q_scale;
+    s->k_scale = d->k_scale;
+    s->v_scale = d->v_scale;
+    s->tau = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
+    return STEM_OK;
+}
+
+int check_kv(const stem_kv_desc *kv, const Shape &s, KvView *out) {
+    if (!kv) return fail(STEM_EINVAL, "kv is NULL");
+    if (!kv->k || !kv->v) return fail(STEM_EINVAL, "k or v is NULL");
+    out->k = kv->k;
+    out->v = kv->v;
+    out->table = kv->block_table;
+    out->page_log2 = 0;
+    out->pages_per_seq = 0;
+    if (kv->block_table) {
+        const int p = kv->page_size;
+        if (p < 1 || (p & (p - 1))) return fail(STEM_EINVAL, "page_size %d is not a power of two", p);
+        if ((long long)kv->pages_per_seq * p < s.seq)
+            return fail(STEM_EINVAL, "pages_per_seq * page_size < seq_len");
+        if (kv->num_pages < 1) return fail(STEM_EINVAL, "num_pages must be positive");
+        int lg = 0;
+        while ((1 << lg) < p) ++lg;
+        out->page_log2 = lg;
+        out->pages_per_seq = kv->pages_per_seq;
+    }
+    return STEM_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(STEM_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Reports an error left by earlier asynchronous work before enqueuing more.
+int hip_precheck() {
+    hipError_t e = hipPeekAtLastError();
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(STEM_EHIP, "earlier HIP error: %s", hipGetErrorString(e));
+    }
+    return STEM_OK;
+}
+
+void workspace_layout(const Shape &s, size_t *qbar, size_t *kbar, size_t *lvn, size_t *total) {
+    const size_t nq = (size_t)s.batch * s.hq * s.nb * s.d * sizeof(float);
+    const size_t nk = (size_t)s.batch * s.hkv * s.nb * s.d * sizeof(float);
+    const size_t nl = (size_t)s.batch * s.hkv * s.nb * sizeof(float);
+    *qbar = 0;
+    *kbar = align256(nq);
+    *lvn = *kbar + align256(nk);
+    *total = *lvn + align256(nl);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *stem_last_error(void) { return g_err; }
+
+int stem_score_workspace_size(const stem_attn_desc *desc, size_t *bytes) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if (!bytes) return fail(STEM_EINVAL, "bytes is NULL");
+    size_t a, b, c;
+    workspace_layout(s, &a, &b, &c, bytes);
+    return ok();
+}
+
+int stem_score(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv, float *scores,
+               void *workspace, size_t workspace_bytes, void *stream) {
+    Shape s;
+    KvView v;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if ((rc = check_kv(kv, s, &v))) return rc;
+    if (!q || !scores || !workspace) return fail(STEM_EINVAL, "q, scores or workspace is NULL");
+    size_t oq, ok_, ol, total;
+    workspace_layout(s, &oq, &ok_, &ol, &total);
+    if (workspace_bytes < total)
+        return fail(STEM_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
+    if ((rc = hip_precheck())) return rc;
+    char *ws = static_cast<char *>(workspace);
+    float *qbar = reinterpret_cast<float *>(ws + oq);
+    float *kbar = reinterpret_cast<float *>(ws + ok_);
+    float *lvn = reinterpret_cast<float *>(ws + ol);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_pool(s, q, v, qbar, kbar, lvn, st);
+    if (e == hipSuccess) e = launch_score(s, qbar, kbar, lvn, scores, st);
+    return hip_status(e, "stem_score launch");
+}
+
+int stem_tpd_budget(int32_t num_blocks, double density, double alpha, int32_t *budget_host,
+                    int64_t *total) {
+    TpdPlan p;
+    const char *why = "";
+    int rc = tpd_make_plan(num_blocks, density, alpha, &p, &why);
+    if (rc) return fail(rc, "%s", why);
+    if (budget_host)
+        for (int i = 0; i < num_blocks; ++i) budget_host[i] = tpd_row_budget(p, i);
+    if (total) *total = p.total;
+    return ok();
+}
+
+int stem_select(const stem_attn_desc *desc, const float *scores, double density, double alpha,
+                uint32_t *mask, int32_t *list, int32_t list_stride, int32_t *count, void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if (!scores || !mask) return fail(STEM_EINVAL, "scores or mask is NULL");
+    TpdPlan p;
+    const char *why = "";
+    if ((rc = tpd_make_plan(s.nb, density, alpha, &p, &why))) return fail(rc, "%s", why);
+    if (list) {
+        int kmax = 0;
+        for (int i = 0; i < s.nb; ++i) { int k = tpd_row_budget(p, i); if (k > kmax) kmax = k; }
+        if (list_stride < kmax)
+            return fail(STEM_EINVAL, "list_stride %d is below the largest budget %d", list_stride, kmax);
+    }
+    if ((rc = hip_precheck())) return rc;
+    hipError_t e = launch_select(s, p, scores, mask, list, list_stride, count,
+                                 static_cast<hipStream_t>(stream));
+    return hip_status(e, "stem_select launch");
+}
+
+int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                const uint32_t *mask, void *o, float *lse, void *stream) {
+    Shape s;
+    KvView v;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if ((rc = check_kv(kv, s, &v))) return rc;
+    if (!q || !o) return fail(STEM_EINVAL, "q or o is NULL");
+    if ((rc = hip_precheck())) return rc;
+    hipError_t e = launch_bsa(s, q, v, mask, o, lse, static_cast<hipStream_t>(stream));
+    return hip_status(e, "bsa_prefill launch");
+}
+
+}  // extern "C"

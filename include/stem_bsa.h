@@ -1,0 +1,158 @@
+/*
+ * stem_bsa.h — C ABI of the Stem block-sparse prefill-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path has three steps, each one entry point:
+ *   stem_score   OAM block scoring: compact per-block Q/K representations, one
+ *                small GEMM per head, plus the log of each V block's norm
+ *                (Stem article on cn486.com, §一.3.2 "Output-Aware Metric" and
+ *                §二.2.1 "Stem operator optimisation").
+ *   stem_select  TPD budget fused with top-k block selection (same article,
+ *                §一.3.1 "Token Position Decay" and §二.2.1; setupai.cc summary
+ *                "Technical Deep Dive").
+ *   bsa_prefill  causal block-sparse flash attention over the kept blocks
+ *                (same article, §二.2.2 "BSA operator optimisation"); with no
+ *                mask it is the dense causal kernel used as the baseline of
+ *                §二.3 "operator benchmark".
+ * stem_tpd_budget exposes the budget on the host.
+ *
+ * Conventions for every entry point
+ *   - Tensors are row-major, in caller-owned DEVICE memory unless a comment
+ *     says "host".  The library never allocates or frees memory and never
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream).
+ *   - Layouts: Q [batch, seq_len, num_q_heads, head_dim];
+ *     contiguous K/V [batch, seq_len, num_kv_heads, head_dim];
+ *     paged K/V [num_pages, page_size, num_kv_heads, head_dim] with
+ *     block_table [batch, pages_per_seq] (token t of sequence b lives in page
+ *     block_table[b][t / page_size], row t % page_size).
+ *   - Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   - Blocks are block_size tokens; Nb = seq_len / block_size.  Positions of
+ *     queries and keys are both 0..seq_len-1 (prefill, causal).
+ *   - Return value: STEM_OK, or a negative stem_status.  On a non-OK return
+ *     nothing has been enqueued; stem_last_error() gives a message (per
+ *     thread).  A HIP error raised by earlier asynchronous work may surface
+ *     as STEM_EHIP on a later call.
+ *   - Calls are thread-safe; calls on one stream execute in order.
+ *
+ * Supported shapes: head_dim in {64, 128}; block_size in {64, 128};
+ * seq_len a positive multiple of block_size with Nb <= 4096; dtype STEM_F32,
+ * STEM_BF16 or STEM_FP8_E4M3 (OCP E4M3, "e4m3fn", with per-tensor fp32
+ * scales: real value = code * scale).  Paged K/V: page_size a power of two.
+ */
+#ifndef STEM_BSA_H
+#define STEM_BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STEM_OK = 0,
+    STEM_EINVAL = -1,        /* invalid argument (null pointer, bad shape or range) */
+    STEM_EUNSUPPORTED = -2,  /* valid but not built (head_dim, block_size, dtype, alpha) */
+    STEM_EHIP = -3,          /* HIP runtime error */
+    STEM_EWORKSPACE = -4     /* workspace smaller than stem_score_workspace_size() */
+} stem_status;
+
+typedef enum {
+    STEM_F32 = 0,
+    STEM_BF16 = 1,
+    STEM_FP8_E4M3 = 2
+} stem_dtype;
+
+/* Problem shape, element type and scales (by value everywhere it is read). */
+typedef struct {
+    int32_t batch;
+    int32_t seq_len;         /* multiple of block_size */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;    /* divides num_q_heads */
+    int32_t head_dim;        /* 64 or 128 */
+    int32_t block_size;      /* 64 or 128 */
+    int32_t dtype;           /* stem_dtype of Q, K and V */
+    float q_scale, k_scale, v_scale;   /* FP8 dequantisation scales; must be 1 otherwise */
+    float softmax_scale;     /* tau; 0 selects 1/sqrt(head_dim) */
+} stem_attn_desc;
+
+/* Where K and V live.  block_table == NULL: contiguous [batch, seq_len,
+ * num_kv_heads, head_dim] tensors; otherwise paged (layout above) and every
+ * block_table entry must lie in [0, num_pages) — entries are not checked on
+ * the device. */
+typedef struct {
+    const void *k;
+    const void *v;
+    const int32_t *block_table;  /* device [batch, pages_per_seq] or NULL */
+    int32_t page_size;           /* power of two; ignored when contiguous */
+    int32_t pages_per_seq;       /* >= seq_len / page_size */
+    int32_t num_pages;
+} stem_kv_desc;
+
+/* Bytes of scratch stem_score needs: the pooled representations it writes
+ * there, each region starting on a 256-byte boundary, in this order:
+ *   qbar [batch, num_q_heads, Nb, head_dim] fp32   mean of each block's Q rows
+ *   kbar [batch, num_kv_heads, Nb, head_dim] fp32  mean of each block's K rows
+ *   lvn  [batch, num_kv_heads, Nb] fp32            ln of the Frobenius norm of the block's V rows
+ * (dequantised values for FP8).  They stay valid after the call. */
+int stem_score_workspace_size(const stem_attn_desc *desc, size_t *bytes);
+
+/* OAM block scores (Stem article §一.3.2, §二.2.1):
+ *   scores[b, h, I, J] = tau * <qbar[b,h,I], kbar[b,g(h),J]> + lvn[b,g(h),J]   for J <= I
+ *   scores[b, h, I, J] = -inf                                                   for J >  I
+ * scores: fp32 [batch, num_q_heads, Nb, Nb].  All arithmetic is fp32 with a
+ * fixed summation order, so repeated calls give identical bits.
+ * workspace: device memory of at least stem_score_workspace_size() bytes. */
+int stem_score(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+               float *scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/* TPD budget on the host (Stem article §一.3.1; setupai.cc "Technical Deep
+ * Dive").  T = floor(density * Nb(Nb+1)/2 + 1/2) computed in double, clamped
+ * to [2*Nb - 1, Nb(Nb+1)/2].  Row 0 keeps 1 block, every other row starts at
+ * 2 (sink and diagonal); the remaining T - (2*Nb - 1) blocks are granted one
+ * at a time to the row I with the smallest (k[I]+1) / (I+1)^(1-alpha) among
+ * rows with k[I] < I+1, equal keys to the smaller I.
+ *   density in (0, 1]; alpha in {0, 0.5, 1} (0: uniform keep ratio, 0.5:
+ *   ratio decaying as 1/sqrt(I+1), 1: uniform count); 1 <= num_blocks <= 65536.
+ *   budget_host: host int32 [num_blocks] (may be NULL); total: host (may be NULL). */
+int stem_tpd_budget(int32_t num_blocks, double density, double alpha,
+                    int32_t *budget_host, int64_t *total);
+
+/* Fused TPD budget + top-k selection (Stem article §二.2.1).  For every row
+ * (b, h, I): keep J = 0 and J = I, then the budget[I] - |{0, I}| best J in
+ * [1, I-1] ordered by score descending, equal scores to the smaller J, NaN
+ * below every number.  The budget is the one stem_tpd_budget returns.
+ *   scores: fp32 [batch, num_q_heads, Nb, Nb] (only J < I is read)
+ *   mask:   uint32 [batch, num_q_heads, Nb, ceil(Nb/32)]; bit J%32 of word
+ *           J/32 set when block J is kept; bits above the diagonal are 0.
+ *   list:   optional int32 [batch, num_q_heads, Nb, list_stride]: the kept J
+ *           in ascending order (entries past count undefined);
+ *           list_stride >= max budget.  NULL to skip.
+ *   count:  optional int32 [batch, num_q_heads, Nb] = budget[I].  NULL to skip. */
+int stem_select(const stem_attn_desc *desc, const float *scores, double density, double alpha,
+                uint32_t *mask, int32_t *list, int32_t list_stride, int32_t *count,
+                void *stream);
+
+/* Causal block-sparse attention (Stem article §二.2.2).  For every query token
+ * i of block I and head h: softmax over the keys of the kept blocks J < I and
+ * the keys j <= i of block I when it is kept; a skipped block counts as -inf
+ * scores.  Bits above the diagonal are ignored.  A row with no kept block
+ * gives O = 0 and LSE = -inf.
+ *   mask: as stem_select writes it, or NULL for dense causal attention (every
+ *         block J <= I; a kernel without any mask logic).
+ *   o:    [batch, seq_len, num_q_heads, head_dim]: fp32 for STEM_F32 inputs,
+ *         bf16 for STEM_BF16 and STEM_FP8_E4M3 inputs.
+ *   lse:  optional fp32 [batch, num_q_heads, seq_len], natural log of the
+ *         softmax denominator of tau * q.k (dequantised); NULL to skip. */
+int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                const uint32_t *mask, void *o, float *lse, void *stream);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char *stem_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STEM_BSA_H */

@@ -1,0 +1,317 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars:
+  * scores: |s_gpu - s_oracle| < 1e-4 on and below the diagonal, exactly -inf
+    above it; pooled representations from the workspace within 1e-5;
+  * masks: bit-exact against the oracle's selection rule applied to the GPU's
+    own fp32 scores (both sides decide on the same values), and against the
+    oracle's fp64 scores except at near-ties (|delta score| < 1e-4);
+  * attention, computed on the oracle's mask: max |O - O_ref| within 1e-2
+    (bf16), 6e-2 (fp8) or 1e-4 (fp32 inputs), beyond the output's own
+    rounding to bf16; LSE within 1e-3 (1e-4 for fp32).
+Small shapes get the whole oracle; the full-size workloads are checked on
+sampled rows.  Every case prints its name before it touches the GPU."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_24_amd as sb
+import oracle
+import workloads as wl
+from gpu_common import (TOL_LSE, TOL_O, TOL_SCORE, mask_bits, near_tie_diff, oracle_qkv,
+                        output_error, problem, run_path, workspace_views, kv_args)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _announce(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+# Small workloads: every (dtype, head_dim, block) instantiation, ragged block
+# counts (not a multiple of 32 or 64), GQA, batch > 1 and paged K/V.
+SMALL = [
+    wl.TINY_2K,
+    wl.Workload("bf16-gqa-ragged-b2", 2, 128 * 70, 8, 2, 128, 128, "bf16"),
+    wl.Workload("fp8-paged-gqa8", 1, 128 * 40, 8, 1, 128, 128, "fp8", paged=True, page_size=64),
+    wl.Workload("bf16-b64-d64", 1, 64 * 100, 4, 4, 64, 64, "bf16", density=0.3),
+    wl.Workload("bf16-b128-d64", 1, 128 * 37, 4, 2, 64, 128, "bf16"),
+    wl.Workload("bf16-b64-d128-paged", 1, 64 * 45, 4, 2, 128, 64, "bf16", paged=True, page_size=16),
+    wl.Workload("fp8-b64-d64", 1, 64 * 50, 4, 2, 64, 64, "fp8"),
+    wl.Workload("fp8-b128-d64", 1, 128 * 33, 2, 2, 64, 128, "fp8"),
+    wl.Workload("fp8-b64-d128", 1, 64 * 41, 4, 1, 128, 64, "fp8", density=0.4),
+    wl.Workload("f32-b128-d128", 1, 128 * 12, 2, 1, 128, 128, "f32"),
+    wl.Workload("f32-b64-d128", 1, 64 * 20, 2, 2, 128, 64, "f32"),
+    wl.Workload("f32-b128-d64-paged", 1, 128 * 10, 2, 1, 64, 128, "f32", paged=True, page_size=128),
+    wl.Workload("bf16-single-block", 1, 128, 2, 1, 128, 128, "bf16"),
+    wl.Workload("bf16-alpha0-dense-ish", 1, 128 * 24, 2, 1, 128, 128, "bf16", density=0.7, alpha=0.0),
+    wl.Workload("bf16-alpha1", 1, 128 * 24, 2, 1, 128, 128, "bf16", density=0.3, alpha=1.0),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sb.lib()
+    yield
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_full_oracle(w):
+    _announce(f"small {w.name}")
+    inp = wl.make_inputs(w, device=DEV)
+    out = run_path(w, inp)
+    q, k, v = oracle_qkv(inp)
+    p = out["p"]
+    nb = w.num_blocks
+
+    # pooled representations
+    qb, kb, lv = oracle.pool_blocks(q, k, v, w.block)
+    gq, gk, gl = (x.cpu().double().numpy() for x in workspace_views(p, out["ws"]))
+    assert np.max(np.abs(gq - qb)) < 1e-5
+    assert np.max(np.abs(gk - kb)) < 1e-5
+    assert np.max(np.abs(gl - lv)) < 1e-5
+
+    # scores
+    s_ref = oracle.oam_scores(q, k, v, w.block)
+    s_gpu = out["scores"].cpu().double().numpy()
+    low = np.tril(np.ones((nb, nb), dtype=bool))
+    assert np.all(s_gpu[..., ~low] == -np.inf)
+    assert np.max(np.abs(s_gpu[..., low] - s_ref[..., low])) < TOL_SCORE
+
+    # selection: exact on the GPU's own scores, near-tie rule on the oracle's
+    budget, total = oracle.tpd_budget(nb, w.density, w.alpha)
+    m_gpu = mask_bits(out["mask"], nb)
+    m_same = oracle.select_blocks(s_gpu, budget)
+    assert np.array_equal(m_gpu, m_same)
+    assert np.all(m_gpu.sum(axis=(2, 3)) == total)
+    cnt = out["count"].cpu().numpy()
+    lst = out["list"].cpu().numpy()
+    for bi in range(w.batch):
+        for h in range(w.hq):
+            for i in range(nb):
+                assert cnt[bi, h, i] == budget[i]
+                assert list(lst[bi, h, i, :budget[i]]) == list(np.nonzero(m_gpu[bi, h, i])[0])
+    differing, bad = near_tie_diff(m_gpu, s_ref, budget)
+    assert not bad, bad[:10]
+
+    # attention on the oracle's mask
+    m_ref = oracle.select_blocks(s_ref, budget)
+    words = torch.from_numpy(oracle.pack_block_mask(m_ref).view(np.int32)).to(DEV)
+    k_, v_, table, page = kv_args(w, inp)
+    o, lse = sb.attention(p, inp["q"], k_, v_, words, table, page)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.block_sparse_attention(q, k, v, m_ref, w.block)
+    assert output_error(o, o_ref) < TOL_O[w.dtype]
+    assert np.max(np.abs(lse.cpu().double().numpy() - lse_ref)) < TOL_LSE[w.dtype]
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[2], SMALL[6]], ids=lambda w: w.name)
+def test_dense_kernel_equals_oracle_and_full_mask(w):
+    _announce(f"dense {w.name}")
+    inp = wl.make_inputs(w, device=DEV)
+    p = problem(w, inp)
+    k_, v_, table, page = kv_args(w, inp)
+    o_d, l_d = sb.attention(p, inp["q"], k_, v_, None, table, page)
+    # density 1 through the selection: every causal block, same arithmetic
+    scores, _ = sb.score(p, inp["q"], k_, v_, table, page)
+    full, _, _ = sb.select(p, scores, 1.0, 0.5)
+    o_s, l_s = sb.attention(p, inp["q"], k_, v_, full, table, page)
+    torch.cuda.synchronize()
+    nb = w.num_blocks
+    assert np.all(mask_bits(full, nb) == np.tril(np.ones((nb, nb), dtype=bool)))
+    assert torch.equal(o_d, o_s) and torch.equal(l_d, l_s)
+    q, k, v = oracle_qkv(inp)
+    o_ref, l_ref = oracle.dense_causal_attention(q, k, v) if w.seq <= 2048 else \
+        oracle.block_sparse_attention(q, k, v, np.ones((w.batch, w.hq, nb, nb), dtype=bool), w.block)
+    assert output_error(o_d, o_ref) < TOL_O[w.dtype]
+    assert np.max(np.abs(l_d.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
+
+
+def test_paged_equals_contiguous_bitwise():
+    w = wl.Workload("paged-vs-contiguous", 1, 128 * 48, 8, 2, 128, 128, "fp8", paged=True, page_size=64)
+    _announce(w.name)
+    inp = wl.make_inputs(w, device=DEV)
+    a = run_path(w, inp, paged=True)
+    b = run_path(w, inp, paged=False)
+    for key in ("scores", "mask", "o", "lse"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_run_twice_bit_identical():
+    w = SMALL[1]
+    _announce("determinism " + w.name)
+    inp = wl.make_inputs(w, device=DEV)
+    a = run_path(w, inp)
+    b = run_path(w, inp)
+    for key in ("scores", "ws", "mask", "list", "count", "o", "lse"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_empty_rows_and_bits_above_diagonal():
+    w = wl.Workload("edge-masks", 1, 128 * 9, 2, 1, 128, 128, "bf16")
+    _announce(w.name)
+    inp = wl.make_inputs(w, device=DEV)
+    p = problem(w, inp)
+    nb = w.num_blocks
+    rng = np.random.default_rng(5)
+    m = np.tril(rng.random((1, 2, nb, nb)) < 0.5)
+    m[0, 0, 4, :] = False                     # an empty row
+    m[0, 1, 0, :] = False                     # the very first row empty
+    words = torch.from_numpy(oracle.pack_block_mask(m).view(np.int32)).to(DEV)
+    o1, l1 = sb.attention(p, inp["q"], inp["k"], inp["v"], words)
+    m2 = m | np.triu(np.ones((nb, nb), dtype=bool), 1)        # junk above the diagonal
+    words2 = torch.from_numpy(oracle.pack_block_mask(m2).view(np.int32)).to(DEV)
+    o2, l2 = sb.attention(p, inp["q"], inp["k"], inp["v"], words2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    q, k, v = oracle_qkv(inp)
+    o_ref, l_ref = oracle.block_sparse_attention(q, k, v, m, w.block)
+    assert output_error(o1, o_ref) < TOL_O["bf16"]
+    lg = l1.cpu().double().numpy()
+    assert np.all(np.isneginf(lg[0, 0, 4 * 128:5 * 128])) and np.all(np.isneginf(lg[0, 1, :128]))
+    fin = np.isfinite(l_ref)
+    assert np.max(np.abs(lg[fin] - l_ref[fin])) < TOL_LSE["bf16"]
+    assert torch.all(o1[0, 4 * 128:5 * 128, 0] == 0) and torch.all(o1[0, :128, 1] == 0)
+
+
+def test_selection_special_values():
+    """Ties, NaN, -inf and +-0 scores go through the selection kernel exactly
+    as the oracle's rule orders them."""
+    _announce("selection special values")
+    nb = 150
+    p = sb.Problem(1, 64 * nb, 3, 1, 64, 64, "bf16")
+    rng = np.random.default_rng(9)
+    s = np.round(rng.standard_normal((1, 3, nb, nb)), 1).astype(np.float32)   # many ties
+    s[0, 1] = 0.0                                                             # all tied
+    s[0, 1, :, ::3] = -0.0
+    s[0, 2, :, 7] = np.nan
+    s[0, 2, :, 11] = -np.inf
+    s[0, 2, :, 13] = np.inf
+    scores = torch.from_numpy(s).to(DEV)
+    for density, alpha in ((0.25, 0.5), (0.1, 0.0), (0.6, 1.0), (1.0, 0.5)):
+        mask, lst, cnt = sb.select(p, scores, density, alpha, with_list=True)
+        torch.cuda.synchronize()
+        budget, _ = oracle.tpd_budget(nb, density, alpha)
+        want = oracle.select_blocks(s.astype(np.float64), budget)
+        assert np.array_equal(mask_bits(mask, nb), want), (density, alpha)
+
+
+def test_zero_value_block():
+    w = wl.Workload("zero-v-block", 1, 128 * 16, 2, 1, 128, 128, "bf16")
+    _announce(w.name)
+    inp = wl.make_inputs(w, device=DEV)
+    inp["v"][:, 3 * 128:4 * 128] = 0
+    out = run_path(w, inp)
+    q, k, v = oracle_qkv(inp)
+    s_gpu = out["scores"].cpu().double().numpy()
+    assert np.all(s_gpu[0, :, 3:, 3] == -np.inf)
+    budget, _ = oracle.tpd_budget(w.num_blocks, w.density, w.alpha)
+    assert np.array_equal(mask_bits(out["mask"], w.num_blocks), oracle.select_blocks(s_gpu, budget))
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the bench times.
+# --------------------------------------------------------------------------
+
+def _sampled_check(w, inp, out, rows_per_head=12, heads=4, seed=0):
+    """Scores of whole sampled heads (oracle, fp64), exact selection on the
+    GPU's scores of those heads, attention on sampled rows with the GPU mask."""
+    nb = w.num_blocks
+    G = w.hq // w.hkv
+    rng = np.random.default_rng(seed)
+    hs = sorted({0, w.hq - 1} | set(int(x) for x in rng.integers(0, w.hq, heads)))
+    q_all, k_all, v_all = inp["q"], inp["k"], inp["v"]
+    budget, total = oracle.tpd_budget(nb, w.density, w.alpha)
+    m_gpu_all = out["mask"]
+    rows = []
+    for h in hs:
+        g = h // G
+        qh = oracle.dequantize(wl.to_float64(q_all[:, :, h:h + 1]), inp["q_scale"])
+        kh = oracle.dequantize(wl.to_float64(k_all[:, :, g:g + 1]), inp["k_scale"])
+        vh = oracle.dequantize(wl.to_float64(v_all[:, :, g:g + 1]), inp["v_scale"])
+        s_ref = oracle.oam_scores(qh, kh, vh, w.block)[:, 0]
+        s_gpu = out["scores"][:, h].cpu().double().numpy()
+        low = np.tril(np.ones((nb, nb), dtype=bool))
+        assert np.max(np.abs(s_gpu[:, low] - s_ref[:, low])) < TOL_SCORE, h
+        m_gpu = mask_bits(m_gpu_all[:, h:h + 1], nb)
+        assert np.array_equal(m_gpu, oracle.select_blocks(s_gpu[:, None], budget)), h
+        assert m_gpu.sum() == w.batch * total
+        toks = {0, w.seq - 1, (nb // 2) * w.block, w.seq - w.block}
+        toks |= set(int(x) for x in rng.integers(0, w.seq, rows_per_head))
+        for t in sorted(toks):
+            rows.append((0, h, t))
+        # attention rows of this head
+        sub = [(0, 0, t) for (_, hh, t) in rows if hh == h]
+        o_ref, l_ref = oracle.attention_rows(qh, kh, vh, m_gpu, w.block, sub)
+        o_g = out["o"][0, [t for (_, _, t) in sub], h]
+        l_g = out["lse"][0, h, [t for (_, _, t) in sub]]
+        assert output_error(o_g, o_ref) < TOL_O[w.dtype], h
+        assert np.max(np.abs(l_g.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype], h
+
+
+@pytest.mark.parametrize("w", [wl.GQA_8K], ids=lambda w: w.name)
+def test_full_8k_whole_oracle(w):
+    _announce(f"full {w.name}")
+    inp = wl.make_inputs(w, device=DEV)
+    out = run_path(w, inp)
+    q, k, v = oracle_qkv(inp)
+    nb = w.num_blocks
+    s_ref = oracle.oam_scores(q, k, v, w.block)
+    s_gpu = out["scores"].cpu().double().numpy()
+    low = np.tril(np.ones((nb, nb), dtype=bool))
+    assert np.max(np.abs(s_gpu[..., low] - s_ref[..., low])) < TOL_SCORE
+    budget, _ = oracle.tpd_budget(nb, w.density, w.alpha)
+    m_gpu = mask_bits(out["mask"], nb)
+    assert np.array_equal(m_gpu, oracle.select_blocks(s_gpu, budget))
+    differing, bad = near_tie_diff(m_gpu, s_ref, budget)
+    print(f"near-tie rows: {differing} of {w.hq * nb}", flush=True)
+    assert not bad, bad[:10]
+    m_ref = oracle.select_blocks(s_ref, budget)
+    words = torch.from_numpy(oracle.pack_block_mask(m_ref).view(np.int32)).to(DEV)
+    o, lse = sb.attention(out["p"], inp["q"], inp["k"], inp["v"], words)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.block_sparse_attention(q, k, v, m_ref, w.block)
+    assert output_error(o, o_ref) < TOL_O[w.dtype]
+    assert np.max(np.abs(lse.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
+
+
+@pytest.mark.parametrize("w", [wl.GQA_64K, wl.GQA_128K_FP8_PAGED, wl.GQA_256K], ids=lambda w: w.name)
+def test_full_size_sampled(w):
+    _announce(f"full {w.name}")
+    inp = wl.make_inputs(w, device=DEV, gen_device=DEV)
+    out = run_path(w, inp)
+    _sampled_check(w, inp, out)
+    # dense kernel on sampled rows
+    p = out["p"]
+    k_, v_, table, page = kv_args(w, inp)
+    o_d, l_d = sb.attention(p, inp["q"], k_, v_, None, table, page)
+    torch.cuda.synchronize()
+    h = w.hq // 3
+    g = h // (w.hq // w.hkv)
+    qh = oracle.dequantize(wl.to_float64(inp["q"][:, :, h:h + 1]), inp["q_scale"])
+    kh = oracle.dequantize(wl.to_float64(inp["k"][:, :, g:g + 1]), inp["k_scale"])
+    vh = oracle.dequantize(wl.to_float64(inp["v"][:, :, g:g + 1]), inp["v_scale"])
+    toks = [0, 1, 127, 128, w.seq // 2 + 5, w.seq - 1]
+    o_ref, l_ref = oracle.attention_rows(qh, kh, vh, None, w.block, [(0, 0, t) for t in toks])
+    assert output_error(o_d[0, toks, h], o_ref) < TOL_O[w.dtype]
+    assert np.max(np.abs(l_d[0, h, toks].cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
+
+
+def test_density_sweep_64k_sampled():
+    """The 64K sweep densities (sparsity 20/50/75/80%) on sampled heads."""
+    base = wl.GQA_64K
+    inp = wl.make_inputs(base, device=DEV, gen_device=DEV)
+    for dens in (0.8, 0.5, 0.2):
+        w = wl.Workload(base.name + f"-d{dens}", base.batch, base.seq, base.hq, base.hkv,
+                        base.head_dim, base.block, base.dtype, density=dens)
+        _announce(w.name)
+        out = run_path(w, inp, density=dens)
+        _sampled_check(w, inp, out, rows_per_head=6, heads=2, seed=int(dens * 10))

@@ -1,0 +1,141 @@
+"""CPU-side checks of the C ABI: the library loads and exports every entry
+point include/stem_bsa.h declares, argument checks fail before anything is
+enqueued, and the host TPD budget equals the oracle's.  No GPU is used: the
+calls below either never reach HIP (invalid arguments) or are host-only
+(stem_tpd_budget)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_24_amd as sb
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)           # never dereferenced: validation fails first
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "stem_bsa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_entry_points_are_exported():
+    names = _header_functions()
+    assert set(names) == set(sb.EXPORTS), names
+    h = sb.lib()
+    for n in names:
+        assert hasattr(h, n), n
+
+
+def _desc(**kw):
+    p = dict(batch=1, seq_len=1024, num_q_heads=4, num_kv_heads=2, head_dim=128, block_size=128,
+             dtype="bf16")
+    p.update(kw)
+    return sb.Problem(**p).desc()
+
+
+def _rc_score(d, kv=None, ws_bytes=1 << 30, scores=FAKE, q=FAKE, ws=FAKE):
+    kv = kv or sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
+    return sb.lib().stem_score(ctypes.byref(d), q, ctypes.byref(kv), scores, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seq_len=1000), sb.STEM_EINVAL),               # not a multiple of the block
+    (dict(num_q_heads=3), sb.STEM_EINVAL),              # not a multiple of kv heads
+    (dict(head_dim=96), sb.STEM_EUNSUPPORTED),
+    (dict(block_size=32), sb.STEM_EUNSUPPORTED),
+    (dict(seq_len=128 * 4097), sb.STEM_EUNSUPPORTED),   # too many blocks
+    (dict(batch=0), sb.STEM_EINVAL),
+    (dict(q_scale=2.0), sb.STEM_EINVAL),                # scales only for fp8
+    (dict(dtype="fp8", k_scale=0.0), sb.STEM_EINVAL),
+    (dict(softmax_scale=-1.0), sb.STEM_EINVAL),
+])
+def test_bad_shapes_rejected_everywhere(kw, code):
+    d = _desc(**kw)
+    assert _rc_score(d) == code
+    assert sb.lib().stem_select(ctypes.byref(d), FAKE, 0.25, 0.5, FAKE, None, 0, None, None) == code
+    kv = sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
+    assert sb.lib().bsa_prefill(ctypes.byref(d), FAKE, ctypes.byref(kv), None, FAKE, None, None) == code
+    assert sb.stem_last_error() != ""
+
+
+def test_bad_dtype_code():
+    d = _desc()
+    d.dtype = 7
+    assert _rc_score(d) == sb.STEM_EINVAL
+
+
+def test_null_pointers_rejected():
+    d = _desc()
+    assert _rc_score(d, q=None) == sb.STEM_EINVAL
+    assert _rc_score(d, scores=None) == sb.STEM_EINVAL
+    assert _rc_score(d, ws=None) == sb.STEM_EINVAL
+    kv = sb.KvDesc(None, 0x1000, None, 0, 0, 0)
+    assert _rc_score(d, kv=kv) == sb.STEM_EINVAL
+    assert sb.lib().stem_score(ctypes.byref(d), FAKE, None, FAKE, FAKE, 1 << 30, None) == sb.STEM_EINVAL
+    assert sb.lib().stem_score(None, FAKE, ctypes.byref(kv), FAKE, FAKE, 1 << 30, None) == sb.STEM_EINVAL
+    assert sb.lib().stem_select(ctypes.byref(d), None, 0.25, 0.5, FAKE, None, 0, None, None) == sb.STEM_EINVAL
+    assert sb.lib().stem_select(ctypes.byref(d), FAKE, 0.25, 0.5, None, None, 0, None, None) == sb.STEM_EINVAL
+    kv = sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
+    assert sb.lib().bsa_prefill(ctypes.byref(d), None, ctypes.byref(kv), None, FAKE, None, None) == sb.STEM_EINVAL
+    assert sb.lib().bsa_prefill(ctypes.byref(d), FAKE, ctypes.byref(kv), None, None, None, None) == sb.STEM_EINVAL
+
+
+def test_workspace_size_and_too_small_workspace():
+    p = sb.Problem(2, 1024, 4, 2, 128, 128, "bf16")
+    n = sb.stem_score_workspace_size(p)
+    nb = 8
+    want = 0
+    for x in (2 * 4 * nb * 128 * 4, 2 * 2 * nb * 128 * 4, 2 * 2 * nb * 4):
+        want += (x + 255) // 256 * 256
+    assert n == want
+    assert _rc_score(p.desc(), ws_bytes=n - 1) == sb.STEM_EWORKSPACE
+
+
+def test_paged_kv_checks():
+    d = _desc()
+    bad_page = sb.KvDesc(0x1000, 0x1000, 0x2000, 48, 32, 64)
+    assert _rc_score(d, kv=bad_page) == sb.STEM_EINVAL
+    short = sb.KvDesc(0x1000, 0x1000, 0x2000, 64, 8, 64)      # 8 * 64 < 1024 tokens
+    assert _rc_score(d, kv=short) == sb.STEM_EINVAL
+    nopages = sb.KvDesc(0x1000, 0x1000, 0x2000, 64, 16, 0)
+    assert _rc_score(d, kv=nopages) == sb.STEM_EINVAL
+
+
+def test_select_rejects_bad_density_alpha_and_list_stride():
+    d = _desc()
+    L = sb.lib()
+    assert L.stem_select(ctypes.byref(d), FAKE, 0.0, 0.5, FAKE, None, 0, None, None) == sb.STEM_EINVAL
+    assert L.stem_select(ctypes.byref(d), FAKE, 1.01, 0.5, FAKE, None, 0, None, None) == sb.STEM_EINVAL
+    assert L.stem_select(ctypes.byref(d), FAKE, 0.5, 0.3, FAKE, None, 0, None, None) == sb.STEM_EUNSUPPORTED
+    budget, _ = sb.stem_tpd_budget(8, 0.5, 0.5)
+    assert L.stem_select(ctypes.byref(d), FAKE, 0.5, 0.5, FAKE, FAKE, max(budget) - 1, None, None) == sb.STEM_EINVAL
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0])
+def test_host_tpd_budget_equals_oracle(alpha):
+    for nb in list(range(1, 40)) + [63, 64, 65, 100, 127, 256, 511, 512]:
+        for dens in (0.01, 0.05, 0.1, 0.2, 0.25, 1 / 3, 0.5, 0.75, 0.8, 0.99, 1.0):
+            got = sb.stem_tpd_budget(nb, dens, alpha)
+            want = oracle.tpd_budget(nb, dens, alpha)
+            assert got == (want[0], want[1]), (nb, dens, alpha)
+
+
+@pytest.mark.parametrize("nb,dens", [(1024, 0.25), (2048, 0.25), (512, 0.2), (4096, 0.1)])
+def test_host_tpd_budget_equals_oracle_large(nb, dens):
+    assert sb.stem_tpd_budget(nb, dens, 0.5) == oracle.tpd_budget(nb, dens, 0.5)
+
+
+def test_tpd_budget_errors():
+    with pytest.raises(sb.StemError):
+        sb.stem_tpd_budget(0, 0.5)
+    with pytest.raises(sb.StemError):
+        sb.stem_tpd_budget(8, -0.1)
+    with pytest.raises(sb.StemError) as e:
+        sb.stem_tpd_budget(8, 0.5, 0.25)
+    assert e.value.code == sb.STEM_EUNSUPPORTED
