@@ -1,0 +1,267 @@
+"""Benchmark of the Stem prefill path on one MI355X.
+
+One step = the whole hot path over one batch: OAM scoring (pool + score
+GEMM), the fused TPD budget + top-k selection, and causal block-sparse
+attention over the kept blocks.  Inputs are resident in HBM before the timed
+region.  The dense causal kernel (the same attention kernel without mask
+logic) is timed separately as the denominator of the density ratio.
+
+Prints one JSON line.  Default workload: 131072 tokens, 64 query / 8 KV heads,
+head_dim 128, 128-token blocks, OCP FP8 E4M3 Q/K/V with per-tensor scales,
+paged K/V (64-token pages, random page order), TPD density 1/4.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_sparse_attention_24_amd as sb  # noqa: E402
+import workloads as wl  # noqa: E402
+
+METRIC = "BSA prefill ms + kept-block TFLOP/s at 25% density, 128K; ratio vs dense"
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {w.name: w for w in wl.ALL}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(nb: int, block: int, kept_blocks: int) -> int:
+    """(query, key) pairs attended per head: full B x B tiles for the kept
+    blocks off the diagonal, the causal triangle for each diagonal block."""
+    return block * block * (kept_blocks - nb) + nb * block * (block + 1) // 2
+
+
+def attn_flops(w: wl.Workload, kept_blocks_per_head: int) -> float:
+    """Algorithmic FLOPs: 2*d for q.k plus 2*d for p*v per visible pair."""
+    return 4.0 * w.head_dim * w.hq * w.batch * visible_pairs(w.num_blocks, w.block, kept_blocks_per_head)
+
+
+def score_bytes(w: wl.Workload) -> float:
+    """Algorithmic HBM bytes of the scoring pass: read Q, K, V once, write the
+    pooled representations and the score matrix (the GEMM re-reads the pooled
+    rows, a few MiB, not counted)."""
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    nb = w.num_blocks
+    read = w.batch * w.seq * (w.hq + 2 * w.hkv) * w.head_dim * es
+    write = 4 * w.batch * nb * ((w.hq + w.hkv) * w.head_dim + w.hkv) + 4 * w.batch * w.hq * nb * nb
+    return float(read + write)
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def cpu_baseline(w: wl.Workload, inp, budget, seconds: float = 15.0):
+    """The oracle, untuned, on the host cores: OAM scores of head 0, the TPD
+    budget, the selection of head 0 and block-sparse attention of head 0 on
+    query blocks sampled evenly over the sequence until about `seconds` of
+    work, reported as kept-block FLOP/s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    G = w.hq // w.hkv
+    t0 = time.perf_counter()
+    qh = oracle.dequantize(wl.to_float64(inp["q"][:1, :, 0:1]), inp["q_scale"])
+    kh = oracle.dequantize(wl.to_float64(inp["k"][:1, :, 0:1]), inp["k_scale"])
+    vh = oracle.dequantize(wl.to_float64(inp["v"][:1, :, 0:1]), inp["v_scale"])
+    t_conv = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    s = oracle.oam_scores(qh, kh, vh, w.block)
+    k_budget, _ = oracle.tpd_budget(w.num_blocks, w.density, w.alpha)
+    mask = oracle.select_blocks(s, k_budget)
+    t_sel = time.perf_counter() - t0
+    nb = w.num_blocks
+    order = []
+    stride = max(1, nb // 64)
+    for start in range(stride):
+        order.extend(range(nb - 1 - start, -1, -stride))
+    flops = 0.0
+    done = 0
+    t_attn = 0.0
+    for i_blk in order:
+        t0 = time.perf_counter()
+        rows = [(0, 0, t) for t in range(i_blk * w.block, (i_blk + 1) * w.block)]
+        oracle.attention_rows(qh, kh, vh, mask, w.block, rows)
+        t_attn += time.perf_counter() - t0
+        kept = int(mask[0, 0, i_blk, :i_blk + 1].sum())
+        flops += 4.0 * w.head_dim * (w.block * w.block * (kept - 1) + w.block * (w.block + 1) // 2)
+        done += 1
+        if t_attn + t_sel > seconds:
+            break
+    # whole-head selection cost is charged pro rata to the sampled blocks
+    t_total = t_attn + t_sel * done / nb
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"head 0 (KV head {0 // G}): OAM scores, TPD budget and selection of all "
+                       f"{nb} rows (time charged pro rata), then block-sparse attention of "
+                       f"{done} of {nb} query blocks spread over the sequence; "
+                       f"{flops / 1e9:.2f} GFLOP in {t_total:.1f} s (+{t_conv:.1f} s fp64 upcast, not charged)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=wl.GQA_128K_FP8_PAGED.name, choices=sorted(WORKLOADS))
+    ap.add_argument("--density", type=float, default=None)
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    if args.density is not None:
+        w = wl.Workload(w.name, w.batch, w.seq, w.hq, w.hkv, w.head_dim, w.block, w.dtype,
+                        density=args.density, alpha=w.alpha, sink=w.sink, paged=w.paged,
+                        page_size=w.page_size, seed=w.seed)
+    dev = "cuda"
+    torch.cuda.init()
+    log(f"[bench] workload {w.name} density {w.density}: generating inputs", )
+    inp = wl.make_inputs(w, device=dev, gen_device=dev)
+    p = sb.Problem(w.batch, w.seq, w.hq, w.hkv, w.head_dim, w.block, w.dtype,
+                   float(inp["q_scale"]), float(inp["k_scale"]), float(inp["v_scale"]))
+    if w.paged:
+        k, v, table, page = inp["k_pages"], inp["v_pages"], inp["block_table"], w.page_size
+    else:
+        k, v, table, page = inp["k"], inp["v"], None, 0
+    q = inp["q"]
+    nb = w.num_blocks
+    budget, total = sb.stem_tpd_budget(nb, w.density, w.alpha)
+    kept_flops = attn_flops(w, total)
+    dense_flops = attn_flops(w, nb * (nb + 1) // 2)
+
+    # buffers (allocated once, outside the timed region)
+    scores = torch.empty((w.batch, w.hq, nb, nb), dtype=torch.float32, device=dev)
+    ws = torch.empty(sb.stem_score_workspace_size(p), dtype=torch.uint8, device=dev)
+    mask = torch.empty((w.batch, w.hq, nb, p.mask_words), dtype=torch.int32, device=dev)
+    odt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    o = torch.empty((w.batch, w.seq, w.hq, w.head_dim), dtype=odt, device=dev)
+    lse = torch.empty((w.batch, w.hq, w.seq), dtype=torch.float32, device=dev)
+
+    t_score, t_select, t_bsa = Timer(), Timer(), Timer()
+
+    def step(timed: bool):
+        if timed:
+            with t_score:
+                sb.stem_score(p, q, k, v, scores, ws, table, page)
+            with t_select:
+                sb.stem_select(p, scores, w.density, w.alpha, mask)
+            with t_bsa:
+                sb.bsa_prefill(p, q, k, v, mask, o, lse, table, page)
+        else:
+            sb.stem_score(p, q, k, v, scores, ws, table, page)
+            sb.stem_select(p, scores, w.density, w.alpha, mask)
+            sb.bsa_prefill(p, q, k, v, mask, o, lse, table, page)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    sc_ms, se_ms, bsa_ms = (sum(t.ms()) / len(t.ms()) for t in (t_score, t_select, t_bsa))
+    log(f"[bench] step {ms_step:.3f} ms: score {sc_ms:.3f} select {se_ms:.3f} bsa {bsa_ms:.3f}")
+
+    result = {
+        "metric": METRIC,
+        "value": kept_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": w.describe(),
+        "stages_ms": {"score": sc_ms, "select": se_ms, "bsa": bsa_ms},
+        "bsa_ms": bsa_ms,
+        "bsa_kept_tflops": kept_flops / (bsa_ms * 1e-3) / 1e12,
+        "kept_tflop_per_step": kept_flops / 1e12,
+        "score_gbs": score_bytes(w) / (sc_ms * 1e-3) / 1e9,
+        "score_hbm_frac": score_bytes(w) / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+    peak = PEAK_TFLOPS[w.dtype]
+    result["roofline"] = {"bound": "mfma", "kernel": "bsa_kernel (sparse)",
+                          "achieved": result["bsa_kept_tflops"], "peak": peak, "unit": "TFLOP/s",
+                          "frac": result["bsa_kept_tflops"] / peak, "traffic": None}
+
+    if not args.no_dense:
+        log(f"[bench] dense baseline and density-1 sparse run, {args.dense_steps} each")
+        full = torch.empty_like(mask)
+        sb.stem_select(p, scores, 1.0, w.alpha, full)
+        t_dense, t_full = Timer(), Timer()
+        sb.bsa_prefill(p, q, k, v, None, o, lse, table, page)
+        for _ in range(args.dense_steps):
+            with t_dense:
+                sb.bsa_prefill(p, q, k, v, None, o, lse, table, page)
+        sb.bsa_prefill(p, q, k, v, full, o, lse, table, page)
+        for _ in range(args.dense_steps):
+            with t_full:
+                sb.bsa_prefill(p, q, k, v, full, o, lse, table, page)
+        torch.cuda.synchronize()
+        dense_ms = sum(t_dense.ms()) / args.dense_steps
+        full_ms = sum(t_full.ms()) / args.dense_steps
+        rho = kept_flops / dense_flops
+        result.update({
+            "dense_ms": dense_ms,
+            "dense_tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+            "ratio_vs_dense": bsa_ms / (w.density * dense_ms),
+            "ratio_vs_dense_rho": bsa_ms / (rho * dense_ms),
+            "skip_overhead_density1": full_ms / dense_ms - 1.0,
+            "density1_sparse_ms": full_ms,
+        })
+        log(f"[bench] dense {dense_ms:.3f} ms, density-1 sparse {full_ms:.3f} ms, "
+            f"R {result['ratio_vs_dense']:.3f}")
+
+    if not args.no_cpu_baseline:
+        log("[bench] oracle CPU baseline (bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(w, inp, budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

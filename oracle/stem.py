@@ -308,9 +308,12 @@ def attention_rows(q, k, v, block_mask, block, rows, softmax_scale=None):
     group = Hq // Hkv
     nb = S // block
     tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    outs, lses = [], []
-    for bi, h, i in rows:
-        i_blk = i // block
+    out_o = np.zeros((len(rows), d))
+    out_l = np.zeros(len(rows))
+    groups = {}                                   # rows of one query block share its keys
+    for n, (bi, h, i) in enumerate(rows):
+        groups.setdefault((bi, h, i // block), []).append(n)
+    for (bi, h, i_blk), members in groups.items():
         if block_mask is None:
             mrow = np.ones(nb, dtype=bool)
         elif callable(block_mask):
@@ -319,13 +322,14 @@ def attention_rows(q, k, v, block_mask, block, rows, softmax_scale=None):
             mrow = block_mask[bi, h, i_blk]
         keys_idx, diag = _visible_keys(mrow, i_blk, block)
         g = h // group
-        qrow = np.asarray(q[bi, i, h], dtype=np.float64)[None, :]
+        pos = np.array([rows[n][2] for n in members])
+        qrows = np.asarray(q[bi, pos, h], dtype=np.float64)
         kk = np.asarray(k[bi, :, g], dtype=np.float64)
         vv = np.asarray(v[bi, :, g], dtype=np.float64)
-        oo, ll = _attend(qrow, np.array([i]), keys_idx, diag, i_blk, block, kk, vv, tau)
-        outs.append(oo[0])
-        lses.append(ll[0])
-    return np.array(outs), np.array(lses)
+        oo, ll = _attend(qrows, pos, keys_idx, diag, i_blk, block, kk, vv, tau)
+        out_o[members] = oo
+        out_l[members] = ll
+    return out_o, out_l
 
 
 def dense_causal_attention(q, k, v, softmax_scale=None):
