@@ -47,8 +47,6 @@ struct BsaArgs {
 template <int DT, int D, int BLK>
 struct Geo {
     static constexpr int ES = DT == kF32 ? 4 : DT == kBF16 ? 2 : 1;
-    static constexpr int NW = BLK / 32;
-    static constexpr int NT = NW * 64;
     static constexpr int KROWB = D * ES;
     static constexpr int KCH = KROWB / 16;
     static constexpr int KSWZ = (KCH < 16 ? KCH : 16) - 1;
@@ -58,12 +56,29 @@ struct Geo {
     static constexpr int VCH = VROWB / 16;
     static constexpr int VSWZ = (VCH < 16 ? VCH : 16) - 1;
     static constexpr int STAGES = (2 * 2 * TILEB <= 128 * 1024) ? 2 : 1;
-    static constexpr int NTILE = BLK / 32;            // 32-key tiles per block
+    // Waves: NWQ groups of 32 query rows; each block's keys are split over
+    // KSPLIT waves per group (partial softmax states merged after the loop),
+    // which puts two waves on every SIMD.
+    static constexpr int KGRAN = DT == kFP8 ? 64 : 32;  // keys of one PV MFMA step group
+    static constexpr int KSPLIT = BLK / 2 >= KGRAN ? 2 : 1;
+    static constexpr int NWQ = BLK / 32;
+    static constexpr int NW = NWQ * KSPLIT;
+    static constexpr int NT = NW * 64;
+    static constexpr int KPW = BLK / KSPLIT;          // keys of a block per wave
+    static constexpr int NTW = KPW / 32;              // 32-key tiles per wave
+    static constexpr int NTILE = BLK / 32;
     static constexpr int NDT = D / 32;                // 32-wide d tiles of O
     static constexpr int NKC = BLK * KCH / NT;        // K 16-byte chunks per thread
     static constexpr int NSUB = BLK * D / 64;         // 8x8 V sub-tiles per block
     static constexpr int NVI = (NSUB + NT - 1) / NT;  // V sub-tiles per thread
+    static constexpr int NVS = VT ? NVI * 8 : NKC;    // V staging registers (u32x4) per thread
     static constexpr int LIST = 4096;                 // max blocks per row
+    static constexpr int COMB = KSPLIT == 2 ? NWQ * 64 * (D / 2) * 4 : 0;   // partial O bytes
+    static constexpr int SMEM = STAGES * 2 * TILEB > COMB ? STAGES * 2 * TILEB : COMB;
+    // Lazy rescaling: the running max only moves when a block's max exceeds it
+    // by more than THRESH (log2 units), so P stays below 2^THRESH.
+    static constexpr float THRESH = 8.0f;
+    static_assert(BLK * KCH % NT == 0, "K chunks must divide over the threads");
 };
 
 // Key (within the block) that MFMA row r of 32-key tile t stands for.
@@ -96,33 +111,29 @@ __device__ __forceinline__ const char *kv_row(const char *base, const BsaArgs &a
     return base + (row * a.hkv + g) * (size_t)(D * ES);
 }
 
-// Registers holding one K (or V) block on its way from HBM to LDS.  K and V
-// are staged at different points of the loop so that only one is live.
+// Registers holding one K and one V block on their way from HBM to LDS:
+// u32x4 k[NKC] and u32x4 v[NVS] per thread (fp8 V uses the low 8 bytes).
 template <class G>
-struct KStage {
-    uint4 k[G::NKC];
-};
-template <int DT, class G>
-struct VStage {
-    uint4 v[DT == kF32 ? G::NKC : G::NVI * 8];        // fp8 uses the low 8 bytes
-};
+using KRegs = u32x4[G::NKC];
+template <class G>
+using VRegs = u32x4[G::NVS];
 
 template <int DT, int D, int BLK, bool PAGED>
-__device__ __forceinline__ void load_k(KStage<Geo<DT, D, BLK>> &st, const BsaArgs &a, int b, int g, int J,
-                                       int tid) {
+__device__ __forceinline__ void load_k(KRegs<Geo<DT, D, BLK>> &st, const BsaArgs &a, int b, int g,
+                                       int J, int tid) {
     using G = Geo<DT, D, BLK>;
     const int tok0 = J * BLK;
 #pragma unroll
     for (int i = 0; i < G::NKC; ++i) {
         const int qid = tid + G::NT * i;
         const int key = qid / G::KCH, c = qid % G::KCH;
-        st.k[i] = *reinterpret_cast<const uint4 *>(kv_row<D, G::ES, PAGED>(a.k, a, b, tok0 + key, g) + c * 16);
+        st[i] = *reinterpret_cast<const u32x4 *>(kv_row<D, G::ES, PAGED>(a.k, a, b, tok0 + key, g) + c * 16);
     }
 }
 
 template <int DT, int D, int BLK, bool PAGED>
-__device__ __forceinline__ void load_v(VStage<DT, Geo<DT, D, BLK>> &st, const BsaArgs &a, int b, int g, int J,
-                                       int tid) {
+__device__ __forceinline__ void load_v(VRegs<Geo<DT, D, BLK>> &st, const BsaArgs &a, int b,
+                                       int g, int J, int tid) {
     using G = Geo<DT, D, BLK>;
     const int tok0 = J * BLK;
     if constexpr (DT == kF32) {
@@ -130,53 +141,53 @@ __device__ __forceinline__ void load_v(VStage<DT, Geo<DT, D, BLK>> &st, const Bs
         for (int i = 0; i < G::NKC; ++i) {
             const int qid = tid + G::NT * i;
             const int key = qid / G::KCH, c = qid % G::KCH;
-            st.v[i] = *reinterpret_cast<const uint4 *>(kv_row<D, G::ES, PAGED>(a.v, a, b, tok0 + key, g) + c * 16);
+            st[i] = *reinterpret_cast<const u32x4 *>(kv_row<D, G::ES, PAGED>(a.v, a, b, tok0 + key, g) + c * 16);
         }
     } else {
 #pragma unroll
         for (int s = 0; s < G::NVI; ++s) {
-            const int sub = tid + G::NT * s;
-            if (sub < G::NSUB) {
-                const int kg = sub % (BLK / 8), dc = sub / (BLK / 8);
+            // threads past the last sub-tile re-load it (unconditional loads keep
+            // the staging in registers); store_v skips them
+            const int sub = min(tid + G::NT * s, G::NSUB - 1);
+            const int kg = sub % (BLK / 8), dc = sub / (BLK / 8);
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const char *p = kv_row<D, G::ES, PAGED>(a.v, a, b, tok0 + 8 * kg + r, g) + dc * 8 * G::ES;
-                    if constexpr (DT == kBF16) {
-                        st.v[8 * s + r] = *reinterpret_cast<const uint4 *>(p);
-                    } else {
-                        const uint2 u = *reinterpret_cast<const uint2 *>(p);
-                        st.v[8 * s + r] = make_uint4(u.x, u.y, 0u, 0u);
-                    }
+            for (int r = 0; r < 8; ++r) {
+                const char *p = kv_row<D, G::ES, PAGED>(a.v, a, b, tok0 + 8 * kg + r, g) + dc * 8 * G::ES;
+                if constexpr (DT == kBF16) {
+                    st[8 * s + r] = *reinterpret_cast<const u32x4 *>(p);
+                } else {
+                    const u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+                    st[8 * s + r] = u32x4{u.x, u.y, 0u, 0u};
                 }
             }
         }
     }
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4 &u, int w) {
+__device__ __forceinline__ uint32_t word_of(const u32x4 &u, int w) {
     return w == 0 ? u.x : w == 1 ? u.y : w == 2 ? u.z : u.w;
 }
 
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void store_k(const KStage<Geo<DT, D, BLK>> &st, char *kl, int tid) {
+__device__ __forceinline__ void store_k(const KRegs<Geo<DT, D, BLK>> &st, char *kl, int tid) {
     using G = Geo<DT, D, BLK>;
 #pragma unroll
     for (int i = 0; i < G::NKC; ++i) {
         const int qid = tid + G::NT * i;
         const int key = qid / G::KCH, c = qid % G::KCH;
-        *reinterpret_cast<uint4 *>(kl + k_off<G>(key, c)) = st.k[i];
+        *reinterpret_cast<u32x4 *>(kl + k_off<G>(key, c)) = st[i];
     }
 }
 
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void store_v(const VStage<DT, Geo<DT, D, BLK>> &st, char *vl, int tid) {
+__device__ __forceinline__ void store_v(const VRegs<Geo<DT, D, BLK>> &st, char *vl, int tid) {
     using G = Geo<DT, D, BLK>;
     if constexpr (DT == kF32) {
 #pragma unroll
         for (int i = 0; i < G::NKC; ++i) {
             const int qid = tid + G::NT * i;
             const int key = qid / G::KCH, c = qid % G::KCH;
-            *reinterpret_cast<uint4 *>(vl + v_off<G>(key, c)) = st.v[i];
+            *reinterpret_cast<u32x4 *>(vl + v_off<G>(key, c)) = st[i];
         }
     } else {
 #pragma unroll
@@ -184,7 +195,7 @@ __device__ __forceinline__ void store_v(const VStage<DT, Geo<DT, D, BLK>> &st, c
             const int sub = tid + G::NT * s;
             if (sub < G::NSUB) {
                 const int kg = sub % (BLK / 8), dc = sub / (BLK / 8);
-                const uint4 *in = &st.v[8 * s];
+                const u32x4 *in = &st[8 * s];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int d = 8 * dc + i;
@@ -192,12 +203,12 @@ __device__ __forceinline__ void store_v(const VStage<DT, Geo<DT, D, BLK>> &st, c
                         // keys 8kg..8kg+7 of column d: pairs of bf16 halves
                         const int w = i >> 1;
                         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-                        uint4 o;
+                        u32x4 o;
                         o.x = __builtin_amdgcn_perm(word_of(in[1], w), word_of(in[0], w), sel);
                         o.y = __builtin_amdgcn_perm(word_of(in[3], w), word_of(in[2], w), sel);
                         o.z = __builtin_amdgcn_perm(word_of(in[5], w), word_of(in[4], w), sel);
                         o.w = __builtin_amdgcn_perm(word_of(in[7], w), word_of(in[6], w), sel);
-                        *reinterpret_cast<uint4 *>(vl + v_off<G>(d, kg)) = o;
+                        *reinterpret_cast<u32x4 *>(vl + v_off<G>(d, kg)) = o;
                     } else {
                         // byte i of each of the 8 key rows
                         const int w = i >> 2, bsel = i & 3;
@@ -206,10 +217,10 @@ __device__ __forceinline__ void store_v(const VStage<DT, Geo<DT, D, BLK>> &st, c
                         const uint32_t x23 = __builtin_amdgcn_perm(word_of(in[3], w), word_of(in[2], w), sel);
                         const uint32_t x45 = __builtin_amdgcn_perm(word_of(in[5], w), word_of(in[4], w), sel);
                         const uint32_t x67 = __builtin_amdgcn_perm(word_of(in[7], w), word_of(in[6], w), sel);
-                        uint2 o;
+                        u32x2 o;
                         o.x = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
                         o.y = __builtin_amdgcn_perm(x67, x45, 0x05040100u);
-                        *reinterpret_cast<uint2 *>(vl + v_off<G>(d, kg >> 1) + ((kg & 1) << 3)) = o;
+                        *reinterpret_cast<u32x2 *>(vl + v_off<G>(d, kg >> 1) + ((kg & 1) << 3)) = o;
                     }
                 }
             }
@@ -221,7 +232,7 @@ __device__ __forceinline__ void store_v(const VStage<DT, Geo<DT, D, BLK>> &st, c
 template <int DT, int D>
 struct QFrag {
     static constexpr int N = DT == kF32 ? D / 2 : DT == kBF16 ? D / 16 : D / 32;
-    uint4 u[DT == kF32 ? 1 : N];
+    u32x4 u[DT == kF32 ? 1 : N];
     float f[DT == kF32 ? N : 1];
 };
 
@@ -233,35 +244,37 @@ __device__ __forceinline__ void load_q(QFrag<DT, D> &qf, const char *qrow, int g
         for (int s = 0; s < D / 2; ++s) qf.f[s] = p[2 * s + g];
     } else if constexpr (DT == kBF16) {
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) qf.u[s] = *reinterpret_cast<const uint4 *>(qrow + (16 * s + 8 * g) * 2);
+        for (int s = 0; s < D / 16; ++s) qf.u[s] = *reinterpret_cast<const u32x4 *>(qrow + (16 * s + 8 * g) * 2);
     } else {
 #pragma unroll
         for (int s = 0; s < D / 64; ++s) {
-            qf.u[2 * s] = *reinterpret_cast<const uint4 *>(qrow + 64 * s + 32 * g);
-            qf.u[2 * s + 1] = *reinterpret_cast<const uint4 *>(qrow + 64 * s + 32 * g + 16);
+            qf.u[2 * s] = *reinterpret_cast<const u32x4 *>(qrow + 64 * s + 32 * g);
+            qf.u[2 * s + 1] = *reinterpret_cast<const u32x4 *>(qrow + 64 * s + 32 * g + 16);
         }
     }
 }
 
+// S^T tile (32 keys of global tile tg x this lane's query) = K Q^T.
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void qk_tile(f32x16 &acc, const QFrag<DT, D> &qf, const char *kl, int t, int lane) {
+__device__ __forceinline__ f32x16 qk_tile(const QFrag<DT, D> &qf, const char *kl, int tg, int lane) {
     using G = Geo<DT, D, BLK>;
     const int r = lane & 31, g = lane >> 5;
-    const int key = keymap<DT>(t, r);
+    const int key = keymap<DT>(tg, r);
+    f32x16 acc = {};
     if constexpr (DT == kBF16) {
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(kl + k_off<G>(key, 2 * s + g));
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(kl + k_off<G>(key, 2 * s + g));
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                           __builtin_bit_cast(bf16x8, qf.u[s]), acc, 0, 0, 0);
         }
     } else if constexpr (DT == kFP8) {
 #pragma unroll
         for (int s = 0; s < D / 64; ++s) {
-            const uint4 a0 = *reinterpret_cast<const uint4 *>(kl + k_off<G>(key, 4 * s + 2 * g));
-            const uint4 a1 = *reinterpret_cast<const uint4 *>(kl + k_off<G>(key, 4 * s + 2 * g + 1));
+            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(kl + k_off<G>(key, 4 * s + 2 * g));
+            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(kl + k_off<G>(key, 4 * s + 2 * g + 1));
             i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            const uint4 b0 = qf.u[2 * s], b1 = qf.u[2 * s + 1];
+            const u32x4 b0 = qf.u[2 * s], b1 = qf.u[2 * s + 1];
             i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
             acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
         }
@@ -273,17 +286,21 @@ __device__ __forceinline__ void qk_tile(f32x16 &acc, const QFrag<DT, D> &qf, con
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf.f[s], acc, 0, 0, 0);
         }
     }
+    return acc;
 }
 
-// O^T[dt] += V^T P^T over the whole block.
+// O^T[dt] += V^T P^T over this wave's keys of the block (tiles t0 .. t0+NTW-1).
+// For FP8 the softmax denominator is accumulated by the MFMA as well (an
+// all-ones row of V^T), so that it sums exactly the quantised P that
+// multiplied V: every lane's lacc[] then holds its query's sum.
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], const f32x16 (&p)[BLK / 32], const char *vl,
-                                         int lane) {
+__device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, const f32x16 (&p)[Geo<DT, D, BLK>::NTW],
+                                         const char *vl, int t0, int lane, int pscale) {
     using G = Geo<DT, D, BLK>;
     const int r = lane & 31, g = lane >> 5;
     if constexpr (DT == kBF16) {
 #pragma unroll
-        for (int t = 0; t < G::NTILE; ++t) {
+        for (int t = 0; t < G::NTW; ++t) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 bf16x8 bv;
@@ -291,39 +308,43 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], const f32x16 (&p)[
                 for (int e = 0; e < 8; ++e) bv[e] = (__bf16)p[t][8 * hh + e];
 #pragma unroll
                 for (int dt = 0; dt < G::NDT; ++dt) {
-                    const uint4 a = *reinterpret_cast<const uint4 *>(vl + v_off<G>(32 * dt + r, 4 * t + 2 * hh + g));
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(vl + v_off<G>(32 * dt + r, 4 * (t0 + t) + 2 * hh + g));
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bv, o[dt], 0, 0, 0);
                 }
             }
         }
     } else if constexpr (DT == kFP8) {
 #pragma unroll
-        for (int pp = 0; pp < G::NTILE / 2; ++pp) {
+        for (int t = 0; t < G::NTW; t += 2) {
+            const int pp = (t0 + t) >> 1;
             i32x8 bv;
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 const int e = 4 * w;
-                const f32x16 &src = p[2 * pp + (e >> 4)];
+                const f32x16 &src = p[t + (e >> 4)];
                 const int ee = e & 15;
-                int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee] * 256.0f, src[ee + 1] * 256.0f, 0, false);
-                x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2] * 256.0f, src[ee + 3] * 256.0f, x, true);
+                int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], 0, false);
+                x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
                 bv[w] = x;
             }
 #pragma unroll
             for (int dt = 0; dt < G::NDT; ++dt) {
                 const int row = 32 * dt + r;
-                const uint4 a0 = *reinterpret_cast<const uint4 *>(vl + v_off<G>(row, 4 * pp + 2 * g));
-                const uint4 a1 = *reinterpret_cast<const uint4 *>(vl + v_off<G>(row, 4 * pp + 2 * g + 1));
+                const u32x4 a0 = *reinterpret_cast<const u32x4 *>(vl + v_off<G>(row, 4 * pp + 2 * g));
+                const u32x4 a1 = *reinterpret_cast<const u32x4 *>(vl + v_off<G>(row, 4 * pp + 2 * g + 1));
                 i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, o[dt], 0, 0, 0, 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, o[dt], 0, 0, 0, 127, 0, pscale);
             }
+            const int one = 0x38383838;                   // four E4M3 1.0
+            const i32x8 ones = {one, one, one, one, one, one, one, one};
+            lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bv, lacc, 0, 0, 0, 127, 0, pscale);
         }
     } else {
 #pragma unroll
-        for (int t = 0; t < G::NTILE; ++t) {
+        for (int t = 0; t < G::NTW; ++t) {
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
-                const int key = keymap<DT>(t, 8 * (vv >> 2) + 4 * g + (vv & 3));
+                const int key = keymap<DT>(t0 + t, 8 * (vv >> 2) + 4 * g + (vv & 3));
 #pragma unroll
                 for (int dt = 0; dt < G::NDT; ++dt) {
                     const int d = 32 * dt + r;
@@ -336,15 +357,19 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], const f32x16 (&p)[
 }
 
 template <int DT, int D, int BLK, bool SPARSE, bool PAGED>
-__global__ __launch_bounds__(2 * BLK, 1) void bsa_kernel(BsaArgs a) {
+__global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a) {
     using G = Geo<DT, D, BLK>;
-    __shared__ __attribute__((aligned(16))) char smem[G::STAGES * 2 * G::TILEB];
+    __shared__ __attribute__((aligned(16))) char smem[G::SMEM];
     __shared__ uint16_t list[SPARSE ? G::LIST : 1];
     __shared__ int wave_sum[G::NW];
+    __shared__ float part_ml[G::KSPLIT == 2 ? 3 * G::NWQ * 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g32 = lane >> 5;
+    const int wq = wave % G::NWQ;                          // query group of this wave
+    const int ks = wave / G::NWQ;                          // key part of this wave
+    const int t0 = ks * G::NTW;                            // its first 32-key tile
 
     // heaviest query blocks first; the heads of one KV group on one XCD
     const int wg = blockIdx.x;
@@ -373,11 +398,12 @@ __global__ __launch_bounds__(2 * BLK, 1) void bsa_kernel(BsaArgs a) {
         if (lane == 63) wave_sum[wave] = incl;
         __syncthreads();
         int base = 0;
-#pragma unroll
-        for (int k = 0; k < G::NW; ++k) base += k < wave ? wave_sum[k] : 0;
         n = 0;
 #pragma unroll
-        for (int k = 0; k < G::NW; ++k) n += wave_sum[k];
+        for (int k = 0; k < G::NW; ++k) {
+            base += k < wave ? wave_sum[k] : 0;
+            n += wave_sum[k];
+        }
         int pos = base + incl - cnt;
         while (w) {
             const int bit = __builtin_ctz(w);
@@ -389,17 +415,19 @@ __global__ __launch_bounds__(2 * BLK, 1) void bsa_kernel(BsaArgs a) {
         n = I + 1;
     }
 
-    const int qrow = 32 * wave + (lane & 31);               // query row in the block
+    const int qrow = 32 * wq + (lane & 31);               // query row in the block
     const int token = I * BLK + qrow;
     if (n == 0) {                                         // nothing visible: O = 0, LSE = -inf
-        if constexpr (DT == kF32) {
-            float *op = reinterpret_cast<float *>(a.o) + (((size_t)b * a.seq + token) * a.hq + h) * D;
-            for (int d = g32; d < D; d += 2) op[d] = 0.0f;
-        } else {
-            uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + (((size_t)b * a.seq + token) * a.hq + h) * D;
-            for (int d = g32; d < D; d += 2) op[d] = 0;
+        if (ks == 0) {
+            if constexpr (DT == kF32) {
+                float *op = reinterpret_cast<float *>(a.o) + (((size_t)b * a.seq + token) * a.hq + h) * D;
+                for (int d = g32; d < D; d += 2) op[d] = 0.0f;
+            } else {
+                uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + (((size_t)b * a.seq + token) * a.hq + h) * D;
+                for (int d = g32; d < D; d += 2) op[d] = 0;
+            }
+            if (a.lse && g32 == 0) a.lse[((size_t)b * a.hq + h) * a.seq + token] = -__builtin_huge_valf();
         }
-        if (a.lse && g32 == 0) a.lse[((size_t)b * a.hq + h) * a.seq + token] = -__builtin_huge_valf();
         return;
     }
 
@@ -408,95 +436,135 @@ __global__ __launch_bounds__(2 * BLK, 1) void bsa_kernel(BsaArgs a) {
 
     f32x16 o[G::NDT];
 #pragma unroll
-    for (int dt = 0; dt < G::NDT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] = 0.0f;
-    float m = -__builtin_huge_valf();
-    float l = 0.0f;
+    for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x16{};
+    const float ninf = -__builtin_huge_valf();
+    float m = ninf;                                       // running max (raw logit units)
+    float l = 0.0f;                                       // this lane's partial sum of P
+    f32x16 lacc = {};                                     // FP8: the sum of P from the MFMA
     const float c = a.c_exp2;
 
-    KStage<G> kst;
-    VStage<DT, G> vst;
+    // Global loads run one full iteration ahead of their use.
+    u32x4 kst[G::NKC];
+    u32x4 vst[G::NVS];
+    load_k<DT, D, BLK, PAGED>(kst, a, b, g, SPARSE ? (int)list[0] : 0, tid);
+    load_v<DT, D, BLK, PAGED>(vst, a, b, g, SPARSE ? (int)list[0] : 0, tid);
+    store_k<DT, D, BLK>(kst, smem, tid);
+    store_v<DT, D, BLK>(vst, smem + G::TILEB, tid);
     {
-        const int J0 = SPARSE ? (int)list[0] : 0;
-        load_k<DT, D, BLK, PAGED>(kst, a, b, g, J0, tid);
-        load_v<DT, D, BLK, PAGED>(vst, a, b, g, J0, tid);
-        store_k<DT, D, BLK>(kst, smem, tid);
-        store_v<DT, D, BLK>(vst, smem + G::TILEB, tid);
+        const int J1 = n > 1 ? (SPARSE ? (int)list[1] : 1) : (SPARSE ? (int)list[0] : 0);
+        load_k<DT, D, BLK, PAGED>(kst, a, b, g, J1, tid);
+        load_v<DT, D, BLK, PAGED>(vst, a, b, g, J1, tid);
     }
     __syncthreads();
 
     for (int it = 0; it < n; ++it) {
         const int J = SPARSE ? (int)list[it] : it;
-        const bool more = it + 1 < n;
-        // the last iteration re-fetches its own block so that loads stay unconditional
-        const int Jn = more ? (SPARSE ? (int)list[it + 1] : it + 1) : J;
         const int cur = G::STAGES == 2 ? (it & 1) : 0;
         const char *kl = smem + cur * 2 * G::TILEB;
         const char *vl = kl + G::TILEB;
-        char *kn = smem + (G::STAGES == 2 ? ((it + 1) & 1) : 0) * 2 * G::TILEB;
-        load_k<DT, D, BLK, PAGED>(kst, a, b, g, Jn, tid);   // in flight during S = K Q^T
 
-        f32x16 s[G::NTILE];
+        f32x16 s[G::NTW];
 #pragma unroll
-        for (int t = 0; t < G::NTILE; ++t) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[t][e] = 0.0f;
-            qk_tile<DT, D, BLK>(s[t], qf, kl, t, lane);
-        }
+        for (int t = 0; t < G::NTW; ++t) s[t] = qk_tile<DT, D, BLK>(qf, kl, t0 + t, lane);
         if (J == I) {                                     // causal mask inside the diagonal block
 #pragma unroll
-            for (int t = 0; t < G::NTILE; ++t)
+            for (int t = 0; t < G::NTW; ++t)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int key = keymap<DT>(t, 8 * (e >> 2) + 4 * g32 + (e & 3));
-                    if (key > qrow) s[t][e] = -__builtin_huge_valf();
+                    const int key = keymap<DT>(t0 + t, 8 * (e >> 2) + 4 * g32 + (e & 3));
+                    if (key > qrow) s[t][e] = ninf;
                 }
         }
-        if constexpr (G::STAGES == 2) {                   // next stage is free: store K, fetch V
-            if (more) store_k<DT, D, BLK>(kst, kn, tid);
-            load_v<DT, D, BLK, PAGED>(vst, a, b, g, Jn, tid);
-        }
-        float mx = -__builtin_huge_valf();
+        float mx = ninf;
 #pragma unroll
-        for (int t = 0; t < G::NTILE; ++t)
+        for (int t = 0; t < G::NTW; ++t)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t][e]);
+            for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[t][e], s[t][e + 1]));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-        const float mc = m_new * c;
+        // lazy rescale: only when some row's max grew by more than THRESH
+        const bool grow = (mx - m) * c > G::THRESH;       // m = -inf: true unless mx = -inf too
+        if (__ballot(grow)) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = m_new == ninf ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * c);
+            m = m_new;
+            l *= alpha;
+            if constexpr (DT == kFP8) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) lacc[e] *= alpha;
+            }
+#pragma unroll
+            for (int dt = 0; dt < G::NDT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        }
+        // FP8: P of this block is cast as P * 2^e with e chosen per query so that
+        // the block's largest P lands in [128, 256); the MFMA multiplies by the
+        // E8M0 scale 2^-e, so every block uses the full E4M3 range.
+        int e = 0;
+        if constexpr (DT == kFP8) {
+            const float x = (mx - m) * c;                     // log2 of the block's largest P
+            e = x > -100.0f ? 8 - (int)ceilf(x) : 100;
+            e = e > 100 ? 100 : e;
+        }
+        const float mc = m == ninf ? 0.0f : m * c - (float)e;
         float ls = 0.0f;
 #pragma unroll
-        for (int t = 0; t < G::NTILE; ++t)
+        for (int t = 0; t < G::NTW; ++t)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(s[t][e], c, -mc));
-                s[t][e] = pe;
+            for (int e2 = 0; e2 < 16; ++e2) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(s[t][e2], c, -mc));
+                s[t][e2] = pe;
                 ls += pe;
             }
-        l = fmaf(l, alpha, ls);
-        m = m_new;
+        l += DT == kFP8 ? ldexpf(ls, -e) : ls;
+        pv_block<DT, D, BLK>(o, lacc, s, vl, t0, lane, 127 - e);
+
+        const bool more = it + 1 < n;
+        if (more) {
+            if constexpr (G::STAGES == 1) __syncthreads();    // the only stage is free again
+            char *kn = smem + (G::STAGES == 2 ? ((it + 1) & 1) : 0) * 2 * G::TILEB;
+            store_k<DT, D, BLK>(kst, kn, tid);
+            store_v<DT, D, BLK>(vst, kn + G::TILEB, tid);
+        }
+        // unconditional (the tail re-fetches its own block): keeps the staging in registers
+        const int J2 = it + 2 < n ? (SPARSE ? (int)list[it + 2] : it + 2) : J;
+        load_k<DT, D, BLK, PAGED>(kst, a, b, g, J2, tid);
+        load_v<DT, D, BLK, PAGED>(vst, a, b, g, J2, tid);
+        if (more) __syncthreads();
+    }
+
+    // ---- merge the key parts, normalise, store --------------------------------
+    l += __shfl_xor(l, 32);                                // exact sum of P: the LSE
+    float lq = DT == kFP8 ? lacc[0] : l;                   // sum of the P that multiplied V
+    if constexpr (G::KSPLIT == 2) {
+        __syncthreads();                                  // stages are free: reuse for partial O
+        float *po = reinterpret_cast<float *>(smem) + wq * 64 * (D / 2);
+        if (ks == 1) {
+#pragma unroll
+            for (int dt = 0; dt < G::NDT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) po[(dt * 16 + e) * 64 + lane] = o[dt][e];
+            part_ml[(3 * wq) * 64 + lane] = m;
+            part_ml[(3 * wq + 1) * 64 + lane] = l;
+            part_ml[(3 * wq + 2) * 64 + lane] = lq;
+        }
+        __syncthreads();
+        if (ks == 1) return;
+        const float m1 = part_ml[(3 * wq) * 64 + lane];
+        const float l1 = part_ml[(3 * wq + 1) * 64 + lane];
+        const float lq1 = part_ml[(3 * wq + 2) * 64 + lane];
+        const float mm = fmaxf(m, m1);
+        const float a0 = m == ninf ? 0.0f : __builtin_amdgcn_exp2f((m - mm) * c);
+        const float a1 = m1 == ninf ? 0.0f : __builtin_amdgcn_exp2f((m1 - mm) * c);
 #pragma unroll
         for (int dt = 0; dt < G::NDT; ++dt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-        pv_block<DT, D, BLK>(o, s, vl, lane);
-
-        if (more) {
-            if constexpr (G::STAGES == 1) {
-                __syncthreads();                          // everyone is done with the only stage
-                store_k<DT, D, BLK>(kst, kn, tid);
-                load_v<DT, D, BLK, PAGED>(vst, a, b, g, Jn, tid);
-            }
-            store_v<DT, D, BLK>(vst, kn + G::TILEB, tid);
-            __syncthreads();
-        }
+            for (int e = 0; e < 16; ++e) o[dt][e] = o[dt][e] * a0 + po[(dt * 16 + e) * 64 + lane] * a1;
+        l = l * a0 + l1 * a1;
+        lq = lq * a0 + lq1 * a1;
+        m = mm;
     }
-
-    // ---- epilogue --------------------------------------------------------------
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv = lt > 0.0f ? a.o_scale / lt : 0.0f;
+    const float inv = lq > 0.0f ? a.o_scale / lq : 0.0f;
     const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < G::NDT; ++dt)
@@ -508,15 +576,15 @@ __global__ __launch_bounds__(2 * BLK, 1) void bsa_kernel(BsaArgs a) {
             if constexpr (DT == kF32) {
                 *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.o) + obase + d0) = f32x4{x0, x1, x2, x3};
             } else {
-                uint2 u;
+                u32x2 u;
                 u.x = f32_to_bf16_bits(x0) | (f32_to_bf16_bits(x1) << 16);
                 u.y = f32_to_bf16_bits(x2) | (f32_to_bf16_bits(x3) << 16);
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = u;
+                *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = u;
             }
         }
     if (a.lse && g32 == 0)
         a.lse[((size_t)b * a.hq + h) * a.seq + token] =
-            lt > 0.0f ? fmaf(m, a.tau_eff, logf(lt)) : -__builtin_huge_valf();
+            l > 0.0f ? fmaf(m, a.tau_eff, logf(l)) : ninf;
 }
 
 template <int DT, int D, int BLK>
@@ -562,7 +630,7 @@ hipError_t launch_bsa(const Shape &s, const void *q, const KvView &kv, const uin
     const float qk = s.q_scale * s.k_scale;
     a.tau_eff = s.tau * qk;
     a.c_exp2 = a.tau_eff * 1.4426950408889634f;
-    a.o_scale = s.dtype == STEM_FP8_E4M3 ? s.v_scale / 256.0f : s.v_scale;
+    a.o_scale = s.v_scale;
     const bool sparse = mask != nullptr;
     switch (s.dtype) {
         case STEM_F32: return launch_dt<kF32>(s, a, sparse, st);
