@@ -46,15 +46,11 @@ struct BsaArgs {
 
 template <int DT, int D, int BLK>
 struct Geo {
+    static constexpr int DTYPE = DT;
     static constexpr int ES = DT == kF32 ? 4 : DT == kBF16 ? 2 : 1;
     static constexpr int KROWB = D * ES;
     static constexpr int KCH = KROWB / 16;
-    static constexpr int KSWZ = (KCH < 16 ? KCH : 16) - 1;
     static constexpr int TILEB = BLK * D * ES;
-    static constexpr bool VT = DT != kF32;            // V stored transposed
-    static constexpr int VROWB = VT ? BLK * ES : D * ES;
-    static constexpr int VCH = VROWB / 16;
-    static constexpr int VSWZ = (VCH < 16 ? VCH : 16) - 1;
     static constexpr int STAGES = (2 * 2 * TILEB <= 128 * 1024) ? 2 : 1;
     // Waves: NWQ groups of 32 query rows; each block's keys are split over
     // KSPLIT waves per group (partial softmax states merged after the loop),
@@ -69,9 +65,6 @@ struct Geo {
     static constexpr int NTILE = BLK / 32;
     static constexpr int NDT = D / 32;                // 32-wide d tiles of O
     static constexpr int NKC = BLK * KCH / NT;        // K 16-byte chunks per thread
-    static constexpr int NSUB = BLK * D / 64;         // 8x8 V sub-tiles per block
-    static constexpr int NVI = (NSUB + NT - 1) / NT;  // V sub-tiles per thread
-    static constexpr int NVS = VT ? NVI * 8 : NKC;    // V staging registers (u32x4) per thread
     static constexpr int LIST = 4096;                 // max blocks per row
     static constexpr int COMB = KSPLIT == 2 ? NWQ * 64 * (D / 2) * 4 : 0;   // partial O bytes
     static constexpr int SMEM = STAGES * 2 * TILEB > COMB ? STAGES * 2 * TILEB : COMB;
@@ -90,142 +83,77 @@ __device__ __forceinline__ int keymap(int t, int r) {
     else return 32 * t + r;
 }
 
+// Chunk swizzle of row `key`: chosen so that the 8 rows a group of 8 lanes
+// feeds to the first MFMA (whose row order keymap() permutes) and the 4 or 8
+// consecutive rows of a transposing read all land on distinct bank groups.
+template <int DT, int KCH>
+__device__ __forceinline__ int swz(int key) {
+    if constexpr (DT == kFP8) return ((key ^ (key >> 3) ^ (key >> 5)) & 7) & (KCH - 1);
+    else if constexpr (DT == kBF16) return ((key ^ ((key >> 3) << 2)) & 7) * (KCH / 8);
+    else return (key & 7) * (KCH / 8);
+}
+
 template <class G>
 __device__ __forceinline__ int k_off(int key, int chunk) {
-    return key * G::KROWB + ((chunk ^ (key & G::KSWZ)) << 4);
-}
-template <class G>
-__device__ __forceinline__ int v_off(int row, int chunk) {
-    return row * G::VROWB + ((chunk ^ (row & G::VSWZ)) << 4);
+    return key * G::KROWB + ((chunk ^ swz<G::DTYPE, G::KCH>(key)) << 4);
 }
 
-template <int D, int ES, bool PAGED>
-__device__ __forceinline__ const char *kv_row(const char *base, const BsaArgs &a, int b, int tok, int g) {
-    size_t row;
-    if constexpr (PAGED) {
-        const int page = a.table[(size_t)b * a.pages_per_seq + (tok >> a.page_log2)];
-        row = ((size_t)page << a.page_log2) + (tok & ((1 << a.page_log2) - 1));
-    } else {
-        row = (size_t)b * a.seq + tok;
-    }
-    return base + (row * a.hkv + g) * (size_t)(D * ES);
-}
-
-// Registers holding one K and one V block on their way from HBM to LDS:
-// u32x4 k[NKC] and u32x4 v[NVS] per thread (fp8 V uses the low 8 bytes).
+// One K or V block: BLK rows of D elements in LDS, row-major, 16-byte chunks
+// XOR-swizzled by row.  Thread `tid` moves chunks tid, tid + NT, ...: a wave
+// covers RPW consecutive rows per step, which never straddle a page (pages are
+// at least 16 tokens), so the page lookup is wave-uniform (a scalar load).
 template <class G>
-using KRegs = u32x4[G::NKC];
-template <class G>
-using VRegs = u32x4[G::NVS];
+using TileRegs = u32x4[G::NKC];
 
 template <int DT, int D, int BLK, bool PAGED>
-__device__ __forceinline__ void load_k(KRegs<Geo<DT, D, BLK>> &st, const BsaArgs &a, int b, int g,
-                                       int J, int tid) {
+__device__ __forceinline__ void load_tile(TileRegs<Geo<DT, D, BLK>> &st, const char *base, const BsaArgs &a,
+                                          int b, int g, int J, int tid) {
     using G = Geo<DT, D, BLK>;
-    const int tok0 = J * BLK;
+    const int tok0 = J * BLK;                              // J is wave-uniform
+    const size_t head = (size_t)g * (D * G::ES);
+    const size_t row_bytes = (size_t)a.hkv * (D * G::ES);
 #pragma unroll
     for (int i = 0; i < G::NKC; ++i) {
         const int qid = tid + G::NT * i;
         const int key = qid / G::KCH, c = qid % G::KCH;
-        st[i] = *reinterpret_cast<const u32x4 *>(kv_row<D, G::ES, PAGED>(a.k, a, b, tok0 + key, g) + c * 16);
-    }
-}
-
-template <int DT, int D, int BLK, bool PAGED>
-__device__ __forceinline__ void load_v(VRegs<Geo<DT, D, BLK>> &st, const BsaArgs &a, int b,
-                                       int g, int J, int tid) {
-    using G = Geo<DT, D, BLK>;
-    const int tok0 = J * BLK;
-    if constexpr (DT == kF32) {
-#pragma unroll
-        for (int i = 0; i < G::NKC; ++i) {
-            const int qid = tid + G::NT * i;
-            const int key = qid / G::KCH, c = qid % G::KCH;
-            st[i] = *reinterpret_cast<const u32x4 *>(kv_row<D, G::ES, PAGED>(a.v, a, b, tok0 + key, g) + c * 16);
+        const int key0 = __builtin_amdgcn_readfirstlane(key);   // first row of this wave's step
+        size_t row0;
+        if constexpr (PAGED) {
+            const int tok = tok0 + key0;
+            const int page = a.table[(size_t)b * a.pages_per_seq + (tok >> a.page_log2)];
+            row0 = ((size_t)page << a.page_log2) + (tok & ((1 << a.page_log2) - 1));
+        } else {
+            row0 = (size_t)b * a.seq + tok0 + key0;
         }
-    } else {
-#pragma unroll
-        for (int s = 0; s < G::NVI; ++s) {
-            // threads past the last sub-tile re-load it (unconditional loads keep
-            // the staging in registers); store_v skips them
-            const int sub = min(tid + G::NT * s, G::NSUB - 1);
-            const int kg = sub % (BLK / 8), dc = sub / (BLK / 8);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const char *p = kv_row<D, G::ES, PAGED>(a.v, a, b, tok0 + 8 * kg + r, g) + dc * 8 * G::ES;
-                if constexpr (DT == kBF16) {
-                    st[8 * s + r] = *reinterpret_cast<const u32x4 *>(p);
-                } else {
-                    const u32x2 u = *reinterpret_cast<const u32x2 *>(p);
-                    st[8 * s + r] = u32x4{u.x, u.y, 0u, 0u};
-                }
-            }
-        }
+        const char *p = base + row0 * row_bytes + head;
+        st[i] = *reinterpret_cast<const u32x4 *>(p + (size_t)(key - key0) * row_bytes + c * 16);
     }
-}
-
-__device__ __forceinline__ uint32_t word_of(const u32x4 &u, int w) {
-    return w == 0 ? u.x : w == 1 ? u.y : w == 2 ? u.z : u.w;
 }
 
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void store_k(const KRegs<Geo<DT, D, BLK>> &st, char *kl, int tid) {
+__device__ __forceinline__ void store_tile(const TileRegs<Geo<DT, D, BLK>> &st, char *tl, int tid) {
     using G = Geo<DT, D, BLK>;
 #pragma unroll
     for (int i = 0; i < G::NKC; ++i) {
         const int qid = tid + G::NT * i;
         const int key = qid / G::KCH, c = qid % G::KCH;
-        *reinterpret_cast<u32x4 *>(kl + k_off<G>(key, c)) = st[i];
+        *reinterpret_cast<u32x4 *>(tl + k_off<G>(key, c)) = st[i];
     }
 }
 
-template <int DT, int D, int BLK>
-__device__ __forceinline__ void store_v(const VRegs<Geo<DT, D, BLK>> &st, char *vl, int tid) {
-    using G = Geo<DT, D, BLK>;
-    if constexpr (DT == kF32) {
-#pragma unroll
-        for (int i = 0; i < G::NKC; ++i) {
-            const int qid = tid + G::NT * i;
-            const int key = qid / G::KCH, c = qid % G::KCH;
-            *reinterpret_cast<u32x4 *>(vl + v_off<G>(key, c)) = st[i];
-        }
-    } else {
-#pragma unroll
-        for (int s = 0; s < G::NVI; ++s) {
-            const int sub = tid + G::NT * s;
-            if (sub < G::NSUB) {
-                const int kg = sub % (BLK / 8), dc = sub / (BLK / 8);
-                const u32x4 *in = &st[8 * s];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int d = 8 * dc + i;
-                    if constexpr (DT == kBF16) {
-                        // keys 8kg..8kg+7 of column d: pairs of bf16 halves
-                        const int w = i >> 1;
-                        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-                        u32x4 o;
-                        o.x = __builtin_amdgcn_perm(word_of(in[1], w), word_of(in[0], w), sel);
-                        o.y = __builtin_amdgcn_perm(word_of(in[3], w), word_of(in[2], w), sel);
-                        o.z = __builtin_amdgcn_perm(word_of(in[5], w), word_of(in[4], w), sel);
-                        o.w = __builtin_amdgcn_perm(word_of(in[7], w), word_of(in[6], w), sel);
-                        *reinterpret_cast<u32x4 *>(vl + v_off<G>(d, kg)) = o;
-                    } else {
-                        // byte i of each of the 8 key rows
-                        const int w = i >> 2, bsel = i & 3;
-                        const uint32_t sel = (uint32_t)bsel | ((uint32_t)(4 + bsel) << 8) | 0x0c0c0000u;
-                        const uint32_t x01 = __builtin_amdgcn_perm(word_of(in[1], w), word_of(in[0], w), sel);
-                        const uint32_t x23 = __builtin_amdgcn_perm(word_of(in[3], w), word_of(in[2], w), sel);
-                        const uint32_t x45 = __builtin_amdgcn_perm(word_of(in[5], w), word_of(in[4], w), sel);
-                        const uint32_t x67 = __builtin_amdgcn_perm(word_of(in[7], w), word_of(in[6], w), sel);
-                        u32x2 o;
-                        o.x = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
-                        o.y = __builtin_amdgcn_perm(x67, x45, 0x05040100u);
-                        *reinterpret_cast<u32x2 *>(vl + v_off<G>(d, kg >> 1) + ((kg & 1) << 3)) = o;
-                    }
-                }
-            }
-        }
-    }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Transposing LDS reads (gfx950).  Within each 16-lane group, source lane s
+// points at a row; ds_read_b64_tr_b8 returns to lane i byte (i % 8) of the
+// rows of source lanes i/8, i/8 + 2, ..., i/8 + 14, and ds_read_b64_tr_b16
+// returns halfword (i % 4) of the rows of source lanes i/4, i/4 + 4, ..., i/4 + 12.
+__device__ __forceinline__ i32x2 lds_tr8(const char *p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(lds_char *)p);
+}
+__device__ __forceinline__ i16x4 lds_tr16(const char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(lds_char *)p);
 }
 
 // Q operand of S^T = K Q^T for this lane's query row.
@@ -298,6 +226,8 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
                                          const char *vl, int t0, int lane, int pscale) {
     using G = Geo<DT, D, BLK>;
     const int r = lane & 31, g = lane >> 5;
+    const int i16 = lane & 15;                            // lane within its 16-lane group
+    const int dhalf = 16 * ((lane >> 4) & 1);             // d offset of the group within a 32-d tile
     if constexpr (DT == kBF16) {
 #pragma unroll
         for (int t = 0; t < G::NTW; ++t) {
@@ -306,10 +236,19 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
                 bf16x8 bv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bv[e] = (__bf16)p[t][8 * hh + e];
+                const int kb = 32 * (t0 + t) + 16 * hh + 8 * g;
 #pragma unroll
                 for (int dt = 0; dt < G::NDT; ++dt) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(vl + v_off<G>(32 * dt + r, 4 * (t0 + t) + 2 * hh + g));
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bv, o[dt], 0, 0, 0);
+                    // V^T operand: 8 consecutive keys at d = 32 dt + (lane & 31), two transposing reads
+                    const int d0 = 32 * dt + dhalf;
+                    const int r0 = kb + (i16 >> 2), r1 = kb + 4 + (i16 >> 2);
+                    const int ch = d0 / 8 + ((i16 & 3) >> 1), off = 8 * (i16 & 1);
+                    const i16x4 v0 = lds_tr16(vl + k_off<G>(r0, ch) + off);
+                    const i16x4 v1 = lds_tr16(vl + k_off<G>(r1, ch) + off);
+                    const i16x4 av0 = v0, av1 = v1;
+                    typedef short i16x8 __attribute__((ext_vector_type(8)));
+                    const i16x8 av = {av0[0], av0[1], av0[2], av0[3], av1[0], av1[1], av1[2], av1[3]};
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, o[dt], 0, 0, 0);
                 }
             }
         }
@@ -327,12 +266,19 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
                 x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
                 bv[w] = x;
             }
+            const int kb = 64 * pp + 32 * g;
 #pragma unroll
             for (int dt = 0; dt < G::NDT; ++dt) {
-                const int row = 32 * dt + r;
-                const u32x4 a0 = *reinterpret_cast<const u32x4 *>(vl + v_off<G>(row, 4 * pp + 2 * g));
-                const u32x4 a1 = *reinterpret_cast<const u32x4 *>(vl + v_off<G>(row, 4 * pp + 2 * g + 1));
-                i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                // V^T operand: 32 consecutive keys at d = 32 dt + (lane & 31), four transposing reads
+                const int d0 = 32 * dt + dhalf;
+                const int ch = d0 / 16, off = 8 * (i16 & 1);
+                i32x8 av;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const i32x2 x = lds_tr8(vl + k_off<G>(kb + 8 * q + (i16 >> 1), ch) + off);
+                    av[2 * q] = x[0];
+                    av[2 * q + 1] = x[1];
+                }
                 o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, o[dt], 0, 0, 0, 127, 0, pscale);
             }
             const int one = 0x38383838;                   // four E4M3 1.0
@@ -348,7 +294,7 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
 #pragma unroll
                 for (int dt = 0; dt < G::NDT; ++dt) {
                     const int d = 32 * dt + r;
-                    const float a = *reinterpret_cast<const float *>(vl + v_off<G>(key, d >> 2) + (d & 3) * 4);
+                    const float a = *reinterpret_cast<const float *>(vl + k_off<G>(key, d >> 2) + (d & 3) * 4);
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[t][vv], o[dt], 0, 0, 0);
                 }
             }
@@ -445,20 +391,21 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
 
     // Global loads run one full iteration ahead of their use.
     u32x4 kst[G::NKC];
-    u32x4 vst[G::NVS];
-    load_k<DT, D, BLK, PAGED>(kst, a, b, g, SPARSE ? (int)list[0] : 0, tid);
-    load_v<DT, D, BLK, PAGED>(vst, a, b, g, SPARSE ? (int)list[0] : 0, tid);
-    store_k<DT, D, BLK>(kst, smem, tid);
-    store_v<DT, D, BLK>(vst, smem + G::TILEB, tid);
+    u32x4 vst[G::NKC];
     {
-        const int J1 = n > 1 ? (SPARSE ? (int)list[1] : 1) : (SPARSE ? (int)list[0] : 0);
-        load_k<DT, D, BLK, PAGED>(kst, a, b, g, J1, tid);
-        load_v<DT, D, BLK, PAGED>(vst, a, b, g, J1, tid);
+        const int J0 = SPARSE ? __builtin_amdgcn_readfirstlane((int)list[0]) : 0;
+        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, b, g, J0, tid);
+        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, b, g, J0, tid);
+        store_tile<DT, D, BLK>(kst, smem, tid);
+        store_tile<DT, D, BLK>(vst, smem + G::TILEB, tid);
+        const int J1 = n > 1 ? (SPARSE ? __builtin_amdgcn_readfirstlane((int)list[1]) : 1) : J0;
+        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, b, g, J1, tid);
+        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, b, g, J1, tid);
     }
     __syncthreads();
 
     for (int it = 0; it < n; ++it) {
-        const int J = SPARSE ? (int)list[it] : it;
+        const int J = SPARSE ? __builtin_amdgcn_readfirstlane((int)list[it]) : it;
         const int cur = G::STAGES == 2 ? (it & 1) : 0;
         const char *kl = smem + cur * 2 * G::TILEB;
         const char *vl = kl + G::TILEB;
@@ -523,13 +470,13 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
         if (more) {
             if constexpr (G::STAGES == 1) __syncthreads();    // the only stage is free again
             char *kn = smem + (G::STAGES == 2 ? ((it + 1) & 1) : 0) * 2 * G::TILEB;
-            store_k<DT, D, BLK>(kst, kn, tid);
-            store_v<DT, D, BLK>(vst, kn + G::TILEB, tid);
+            store_tile<DT, D, BLK>(kst, kn, tid);
+            store_tile<DT, D, BLK>(vst, kn + G::TILEB, tid);
         }
         // unconditional (the tail re-fetches its own block): keeps the staging in registers
-        const int J2 = it + 2 < n ? (SPARSE ? (int)list[it + 2] : it + 2) : J;
-        load_k<DT, D, BLK, PAGED>(kst, a, b, g, J2, tid);
-        load_v<DT, D, BLK, PAGED>(vst, a, b, g, J2, tid);
+        const int J2 = it + 2 < n ? (SPARSE ? __builtin_amdgcn_readfirstlane((int)list[it + 2]) : it + 2) : J;
+        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, b, g, J2, tid);
+        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, b, g, J2, tid);
         if (more) __syncthreads();
     }
 
