@@ -422,6 +422,7 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
                     if (key > qrow) s[t][e] = ninf;
                 }
         }
+        // (NaN never arises: -inf - -inf is kept out of every expression below)
         float mx = ninf;
 #pragma unroll
         for (int t = 0; t < G::NTW; ++t)
@@ -429,10 +430,10 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
             for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[t][e], s[t][e + 1]));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         // lazy rescale: only when some row's max grew by more than THRESH
-        const bool grow = (mx - m) * c > G::THRESH;       // m = -inf: true unless mx = -inf too
+        const bool grow = m == ninf ? mx != ninf : (mx - m) * c > G::THRESH;
         if (__ballot(grow)) {
             const float m_new = fmaxf(m, mx);
-            const float alpha = m_new == ninf ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * c);
+            const float alpha = m == ninf ? (m_new == ninf ? 1.0f : 0.0f) : __builtin_amdgcn_exp2f((m - m_new) * c);
             m = m_new;
             l *= alpha;
             if constexpr (DT == kFP8) {
@@ -445,24 +446,24 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
                 for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
         }
         // FP8: P of this block is cast as P * 2^e with e chosen per query so that
-        // the block's largest P lands in [128, 256); the MFMA multiplies by the
+        // the block's largest P lands in (128, 256]; the MFMA multiplies by the
         // E8M0 scale 2^-e, so every block uses the full E4M3 range.
         int e = 0;
         if constexpr (DT == kFP8) {
-            const float x = (mx - m) * c;                     // log2 of the block's largest P
-            e = x > -100.0f ? 8 - (int)ceilf(x) : 100;
-            e = e > 100 ? 100 : e;
+            const float x = (mx == ninf || m == ninf) ? -1000.0f : (mx - m) * c;   // log2 of the largest P
+            e = 8 - (int)ceilf(fmaxf(x, -92.0f));           // e in [0, 100]
         }
         const float mc = m == ninf ? 0.0f : m * c - (float)e;
-        float ls = 0.0f;
+        float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};            // four partial sums: short add chains
 #pragma unroll
         for (int t = 0; t < G::NTW; ++t)
 #pragma unroll
             for (int e2 = 0; e2 < 16; ++e2) {
                 const float pe = __builtin_amdgcn_exp2f(fmaf(s[t][e2], c, -mc));
                 s[t][e2] = pe;
-                ls += pe;
+                ls4[e2 & 3] += pe;
             }
+        const float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
         l += DT == kFP8 ? ldexpf(ls, -e) : ls;
         pv_block<DT, D, BLK>(o, lacc, s, vl, t0, lane, 127 - e);
 
