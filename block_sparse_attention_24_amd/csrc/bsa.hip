@@ -23,6 +23,8 @@
 //     block's global loads are in flight while the current one is computed.
 //   * bf16: v_mfma_f32_32x32x16_bf16; fp8 (OCP E4M3): v_mfma_f32_32x32x64_f8f6f4
 //     with P scaled by 256 before its fp8 cast; fp32: v_mfma_f32_32x32x2f32.
+#include <type_traits>
+
 #include "device_common.h"
 #include "stem_internal.h"
 
@@ -105,40 +107,61 @@ __device__ __forceinline__ int k_off(int key, int chunk) {
 template <class G>
 using TileRegs = u32x4[G::NKC];
 
-template <int DT, int D, int BLK, bool PAGED>
-__device__ __forceinline__ void load_tile(TileRegs<Geo<DT, D, BLK>> &st, const char *base, const BsaArgs &a,
-                                          int b, int g, int J, int tid) {
+// Loop-invariant part of a thread's tile traffic: for each of its chunks the
+// row offset from the first row its wave covers, and the swizzled LDS offset.
+template <class G>
+struct TileMap {
+    int key0[G::NKC];       // first row of the wave's step (wave-uniform)
+    int voff[G::NKC];       // byte offset of the thread's chunk from that row
+    int loff[G::NKC];       // LDS byte offset of the chunk within a tile
+};
+
+template <int DT, int D, int BLK>
+__device__ __forceinline__ void tile_map(TileMap<Geo<DT, D, BLK>> &tm, const BsaArgs &a, int tid) {
     using G = Geo<DT, D, BLK>;
-    const int tok0 = J * BLK;                              // J is wave-uniform
-    const size_t head = (size_t)g * (D * G::ES);
-    const size_t row_bytes = (size_t)a.hkv * (D * G::ES);
+    const int row_bytes = a.hkv * (D * G::ES);
 #pragma unroll
     for (int i = 0; i < G::NKC; ++i) {
         const int qid = tid + G::NT * i;
         const int key = qid / G::KCH, c = qid % G::KCH;
-        const int key0 = __builtin_amdgcn_readfirstlane(key);   // first row of this wave's step
+        tm.key0[i] = __builtin_amdgcn_readfirstlane(key);
+        tm.voff[i] = (key - tm.key0[i]) * row_bytes + c * 16;
+        tm.loff[i] = k_off<G>(key, c);
+    }
+}
+
+// Global -> registers for block J (wave-uniform).  The row pointer of each
+// wave step is scalar (page lookup included); the per-thread offset is added
+// by a buffer load, so no vector address arithmetic remains.
+template <int DT, int D, int BLK, bool PAGED>
+__device__ __forceinline__ void load_tile(TileRegs<Geo<DT, D, BLK>> &st, const char *base, const BsaArgs &a,
+                                          const TileMap<Geo<DT, D, BLK>> &tm, int b, int g, int J) {
+    using G = Geo<DT, D, BLK>;
+    const int tok0 = J * BLK;
+    const size_t row_bytes = (size_t)a.hkv * (D * G::ES);
+    const size_t head = (size_t)g * (D * G::ES);
+#pragma unroll
+    for (int i = 0; i < G::NKC; ++i) {
         size_t row0;
         if constexpr (PAGED) {
-            const int tok = tok0 + key0;
+            const int tok = tok0 + tm.key0[i];
             const int page = a.table[(size_t)b * a.pages_per_seq + (tok >> a.page_log2)];
             row0 = ((size_t)page << a.page_log2) + (tok & ((1 << a.page_log2) - 1));
         } else {
-            row0 = (size_t)b * a.seq + tok0 + key0;
+            row0 = (size_t)b * a.seq + tok0 + tm.key0[i];
         }
         const char *p = base + row0 * row_bytes + head;
-        st[i] = *reinterpret_cast<const u32x4 *>(p + (size_t)(key - key0) * row_bytes + c * 16);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, 0x7fffffff, 0x00020000);
+        st[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, tm.voff[i], 0, 0));
     }
 }
 
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void store_tile(const TileRegs<Geo<DT, D, BLK>> &st, char *tl, int tid) {
+__device__ __forceinline__ void store_tile(const TileRegs<Geo<DT, D, BLK>> &st, char *tl,
+                                           const TileMap<Geo<DT, D, BLK>> &tm) {
     using G = Geo<DT, D, BLK>;
 #pragma unroll
-    for (int i = 0; i < G::NKC; ++i) {
-        const int qid = tid + G::NT * i;
-        const int key = qid / G::KCH, c = qid % G::KCH;
-        *reinterpret_cast<u32x4 *>(tl + k_off<G>(key, c)) = st[i];
-    }
+    for (int i = 0; i < G::NKC; ++i) *reinterpret_cast<u32x4 *>(tl + tm.loff[i]) = st[i];
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -262,7 +285,8 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
                 const int e = 4 * w;
                 const f32x16 &src = p[t + (e >> 4)];
                 const int ee = e & 15;
-                int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], 0, false);
+                // the high half is written next: its old contents do not matter
+                int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], __builtin_nondeterministic_value(0), false);
                 x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
                 bv[w] = x;
             }
@@ -389,25 +413,31 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
     f32x16 lacc = {};                                     // FP8: the sum of P from the MFMA
     const float c = a.c_exp2;
 
-    // Global loads run one full iteration ahead of their use.
+    // Global loads run one full iteration ahead of their use.  The loop is
+    // unrolled over the two LDS stages so that stage offsets are immediates.
+    TileMap<G> tm;
+    tile_map<DT, D, BLK>(tm, a, tid);
     u32x4 kst[G::NKC];
     u32x4 vst[G::NKC];
+    auto list_at = [&](int i) { return SPARSE ? __builtin_amdgcn_readfirstlane((int)list[i]) : i; };
     {
-        const int J0 = SPARSE ? __builtin_amdgcn_readfirstlane((int)list[0]) : 0;
-        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, b, g, J0, tid);
-        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, b, g, J0, tid);
-        store_tile<DT, D, BLK>(kst, smem, tid);
-        store_tile<DT, D, BLK>(vst, smem + G::TILEB, tid);
-        const int J1 = n > 1 ? (SPARSE ? __builtin_amdgcn_readfirstlane((int)list[1]) : 1) : J0;
-        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, b, g, J1, tid);
-        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, b, g, J1, tid);
+        const int J0 = list_at(0);
+        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, tm, b, g, J0);
+        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, tm, b, g, J0);
+        store_tile<DT, D, BLK>(kst, smem, tm);
+        store_tile<DT, D, BLK>(vst, smem + G::TILEB, tm);
+        const int J1 = n > 1 ? list_at(1) : J0;
+        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, tm, b, g, J1);
+        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, tm, b, g, J1);
     }
     __syncthreads();
 
-    for (int it = 0; it < n; ++it) {
-        const int J = SPARSE ? __builtin_amdgcn_readfirstlane((int)list[it]) : it;
-        const int cur = G::STAGES == 2 ? (it & 1) : 0;
-        const char *kl = smem + cur * 2 * G::TILEB;
+    auto body = [&](auto stage, int it) {
+        constexpr int CUR = decltype(stage)::value;
+        constexpr int NXT = G::STAGES == 2 ? 1 - CUR : 0;
+        const int J = list_at(it);
+        const int J2 = it + 2 < n ? list_at(it + 2) : J;   // the tail re-fetches its own block
+        const char *kl = smem + CUR * 2 * G::TILEB;
         const char *vl = kl + G::TILEB;
 
         f32x16 s[G::NTW];
@@ -470,15 +500,17 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
         const bool more = it + 1 < n;
         if (more) {
             if constexpr (G::STAGES == 1) __syncthreads();    // the only stage is free again
-            char *kn = smem + (G::STAGES == 2 ? ((it + 1) & 1) : 0) * 2 * G::TILEB;
-            store_tile<DT, D, BLK>(kst, kn, tid);
-            store_tile<DT, D, BLK>(vst, kn + G::TILEB, tid);
+            char *kn = smem + NXT * 2 * G::TILEB;
+            store_tile<DT, D, BLK>(kst, kn, tm);
+            store_tile<DT, D, BLK>(vst, kn + G::TILEB, tm);
         }
-        // unconditional (the tail re-fetches its own block): keeps the staging in registers
-        const int J2 = it + 2 < n ? (SPARSE ? __builtin_amdgcn_readfirstlane((int)list[it + 2]) : it + 2) : J;
-        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, b, g, J2, tid);
-        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, b, g, J2, tid);
+        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, tm, b, g, J2);
+        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, tm, b, g, J2);
         if (more) __syncthreads();
+    };
+    for (int it = 0; it < n; it += 2) {
+        body(std::integral_constant<int, 0>{}, it);
+        if (it + 1 < n) body(std::integral_constant<int, G::STAGES == 2 ? 1 : 0>{}, it + 1);
     }
 
     // ---- merge the key parts, normalise, store --------------------------------
