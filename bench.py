@@ -141,6 +141,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy first (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -191,6 +193,13 @@ def main():
             sb.stem_select(p, scores, w.density, w.alpha, mask)
             sb.bsa_prefill(p, q, k, v, mask, o, lse, table, page)
 
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copied 1 GiB (counter calibration)")
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step(False)
