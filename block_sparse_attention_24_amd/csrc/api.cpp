@@ -201,6 +201,15 @@ int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *k
     if (rc) return rc;
     if ((rc = check_kv(kv, s, &v))) return rc;
     if (!q || !o) return fail(STEM_EINVAL, "q or o is NULL");
+    {
+        // the attention kernel addresses K and V with 32-bit buffer offsets
+        const size_t es = s.dtype == STEM_F32 ? 4 : s.dtype == STEM_BF16 ? 2 : 1;
+        const size_t rows = v.table ? (size_t)kv->num_pages * kv->page_size : (size_t)s.batch * s.seq;
+        if (rows * s.hkv * s.d * es >= (size_t(1) << 32))
+            return fail(STEM_EUNSUPPORTED, "K/V tensors of 4 GiB or more are not supported");
+        if (v.table && kv->page_size < 16)
+            return fail(STEM_EUNSUPPORTED, "page_size below 16 tokens is not supported");
+    }
     if ((rc = hip_precheck())) return rc;
     hipError_t e = launch_bsa(s, q, v, mask, o, lse, static_cast<hipStream_t>(stream));
     return hip_status(e, "bsa_prefill launch");

@@ -108,12 +108,13 @@ template <class G>
 using TileRegs = u32x4[G::NKC];
 
 // Loop-invariant part of a thread's tile traffic: for each of its chunks the
-// row offset from the first row its wave covers, and the swizzled LDS offset.
+// first row its wave covers (wave-uniform), the byte offset of the thread's
+// chunk from that row, and the swizzled LDS offset of the chunk.
 template <class G>
 struct TileMap {
-    int key0[G::NKC];       // first row of the wave's step (wave-uniform)
-    int voff[G::NKC];       // byte offset of the thread's chunk from that row
-    int loff[G::NKC];       // LDS byte offset of the chunk within a tile
+    int key0[G::NKC];
+    int voff[G::NKC];
+    int loff[G::NKC];
 };
 
 template <int DT, int D, int BLK>
@@ -130,30 +131,46 @@ __device__ __forceinline__ void tile_map(TileMap<Geo<DT, D, BLK>> &tm, const Bsa
     }
 }
 
-// Global -> registers for block J (wave-uniform).  The row pointer of each
-// wave step is scalar (page lookup included); the per-thread offset is added
-// by a buffer load, so no vector address arithmetic remains.
+// Scalar byte offsets (from the start of the K or V tensor; both have the same
+// layout) of the rows each wave step of block J starts at.  Paged: one
+// wave-uniform page lookup per step.
+template <class G>
+struct BlockOffs {
+    int s[G::NKC];
+};
+
 template <int DT, int D, int BLK, bool PAGED>
-__device__ __forceinline__ void load_tile(TileRegs<Geo<DT, D, BLK>> &st, const char *base, const BsaArgs &a,
-                                          const TileMap<Geo<DT, D, BLK>> &tm, int b, int g, int J) {
+__device__ __forceinline__ BlockOffs<Geo<DT, D, BLK>> block_offs(const BsaArgs &a, const TileMap<Geo<DT, D, BLK>> &tm,
+                                                                 int b, int g, int J) {
     using G = Geo<DT, D, BLK>;
-    const int tok0 = J * BLK;
-    const size_t row_bytes = (size_t)a.hkv * (D * G::ES);
-    const size_t head = (size_t)g * (D * G::ES);
+    BlockOffs<G> bo;
+    const unsigned row_bytes = (unsigned)a.hkv * (D * G::ES);
+    const unsigned head = (unsigned)g * (D * G::ES);
 #pragma unroll
     for (int i = 0; i < G::NKC; ++i) {
-        size_t row0;
+        const int tok = J * BLK + tm.key0[i];
+        unsigned row;
         if constexpr (PAGED) {
-            const int tok = tok0 + tm.key0[i];
-            const int page = a.table[(size_t)b * a.pages_per_seq + (tok >> a.page_log2)];
-            row0 = ((size_t)page << a.page_log2) + (tok & ((1 << a.page_log2) - 1));
+            const int page = a.table[b * a.pages_per_seq + (tok >> a.page_log2)];
+            row = ((unsigned)page << a.page_log2) | (unsigned)(tok & ((1 << a.page_log2) - 1));
         } else {
-            row0 = (size_t)b * a.seq + tok0 + tm.key0[i];
+            row = (unsigned)(b * a.seq + tok);
         }
-        const char *p = base + row0 * row_bytes + head;
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, 0x7fffffff, 0x00020000);
-        st[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, tm.voff[i], 0, 0));
+        bo.s[i] = (int)(row * row_bytes + head);
     }
+    return bo;
+}
+
+// Global -> registers: buffer loads with a constant descriptor for the whole
+// tensor (smaller than 4 GiB, checked on the host), the scalar row offset of
+// the wave step and the loop-invariant per-thread offset.
+template <int DT, int D, int BLK>
+__device__ __forceinline__ void load_tile(TileRegs<Geo<DT, D, BLK>> &st, __amdgpu_buffer_rsrc_t rsrc,
+                                          const BlockOffs<Geo<DT, D, BLK>> &bo, const TileMap<Geo<DT, D, BLK>> &tm) {
+    using G = Geo<DT, D, BLK>;
+#pragma unroll
+    for (int i = 0; i < G::NKC; ++i)
+        st[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, tm.voff[i], bo.s[i], 0));
 }
 
 template <int DT, int D, int BLK>
@@ -241,11 +258,49 @@ __device__ __forceinline__ f32x16 qk_tile(const QFrag<DT, D> &qf, const char *kl
 }
 
 // O^T[dt] += V^T P^T over this wave's keys of the block (tiles t0 .. t0+NTW-1).
+// P of this wave's keys of one block, packed as the B operand of the PV MFMAs.
+template <int DT, int D, int BLK>
+struct PPack {
+    static constexpr int NTW = Geo<DT, D, BLK>::NTW;
+    i32x8 f8[DT == kFP8 ? NTW / 2 : 1];       // 64 keys per FP8 MFMA step
+    bf16x8 b16[DT == kBF16 ? 2 * NTW : 1];    // 16 keys per BF16 MFMA step
+    f32x16 f32[DT == kF32 ? NTW : 1];         // one key pair per FP32 MFMA step
+};
+
+template <int DT, int D, int BLK>
+__device__ __forceinline__ void pack_p(PPack<DT, D, BLK> &pk, const f32x16 (&p)[Geo<DT, D, BLK>::NTW]) {
+    using G = Geo<DT, D, BLK>;
+    if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int t = 0; t < G::NTW; ++t)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pk.b16[2 * t + hh][e] = (__bf16)p[t][8 * hh + e];
+    } else if constexpr (DT == kFP8) {
+#pragma unroll
+        for (int t = 0; t < G::NTW; t += 2)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const int e = 4 * w;
+                const f32x16 &src = p[t + (e >> 4)];
+                const int ee = e & 15;
+                // the high half is written next: its old contents do not matter
+                int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], __builtin_nondeterministic_value(0), false);
+                pk.f8[t >> 1][w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
+            }
+    } else {
+#pragma unroll
+        for (int t = 0; t < G::NTW; ++t) pk.f32[t] = p[t];
+    }
+}
+
+// O^T[dt] += V^T P^T over this wave's keys of the block (tiles t0 .. t0+NTW-1).
 // For FP8 the softmax denominator is accumulated by the MFMA as well (an
 // all-ones row of V^T), so that it sums exactly the quantised P that
 // multiplied V: every lane's lacc[] then holds its query's sum.
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, const f32x16 (&p)[Geo<DT, D, BLK>::NTW],
+__device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, const PPack<DT, D, BLK> &pk,
                                          const char *vl, int t0, int lane, int pscale) {
     using G = Geo<DT, D, BLK>;
     const int r = lane & 31, g = lane >> 5;
@@ -256,9 +311,6 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
         for (int t = 0; t < G::NTW; ++t) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                bf16x8 bv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bv[e] = (__bf16)p[t][8 * hh + e];
                 const int kb = 32 * (t0 + t) + 16 * hh + 8 * g;
 #pragma unroll
                 for (int dt = 0; dt < G::NDT; ++dt) {
@@ -268,10 +320,10 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
                     const int ch = d0 / 8 + ((i16 & 3) >> 1), off = 8 * (i16 & 1);
                     const i16x4 v0 = lds_tr16(vl + k_off<G>(r0, ch) + off);
                     const i16x4 v1 = lds_tr16(vl + k_off<G>(r1, ch) + off);
-                    const i16x4 av0 = v0, av1 = v1;
                     typedef short i16x8 __attribute__((ext_vector_type(8)));
-                    const i16x8 av = {av0[0], av0[1], av0[2], av0[3], av1[0], av1[1], av1[2], av1[3]};
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, o[dt], 0, 0, 0);
+                    const i16x8 av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk.b16[2 * t + hh],
+                                                                    o[dt], 0, 0, 0);
                 }
             }
         }
@@ -279,17 +331,6 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
 #pragma unroll
         for (int t = 0; t < G::NTW; t += 2) {
             const int pp = (t0 + t) >> 1;
-            i32x8 bv;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const int e = 4 * w;
-                const f32x16 &src = p[t + (e >> 4)];
-                const int ee = e & 15;
-                // the high half is written next: its old contents do not matter
-                int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], __builtin_nondeterministic_value(0), false);
-                x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
-                bv[w] = x;
-            }
             const int kb = 64 * pp + 32 * g;
 #pragma unroll
             for (int dt = 0; dt < G::NDT; ++dt) {
@@ -303,11 +344,11 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
                     av[2 * q] = x[0];
                     av[2 * q + 1] = x[1];
                 }
-                o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, o[dt], 0, 0, 0, 127, 0, pscale);
+                o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pk.f8[t >> 1], o[dt], 0, 0, 0, 127, 0, pscale);
             }
             const int one = 0x38383838;                   // four E4M3 1.0
             const i32x8 ones = {one, one, one, one, one, one, one, one};
-            lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bv, lacc, 0, 0, 0, 127, 0, pscale);
+            lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pk.f8[t >> 1], lacc, 0, 0, 0, 127, 0, pscale);
         }
     } else {
 #pragma unroll
@@ -319,7 +360,7 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
                 for (int dt = 0; dt < G::NDT; ++dt) {
                     const int d = 32 * dt + r;
                     const float a = *reinterpret_cast<const float *>(vl + k_off<G>(key, d >> 2) + (d & 3) * 4);
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[t][vv], o[dt], 0, 0, 0);
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pk.f32[t][vv], o[dt], 0, 0, 0);
                 }
             }
         }
@@ -413,104 +454,135 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
     f32x16 lacc = {};                                     // FP8: the sum of P from the MFMA
     const float c = a.c_exp2;
 
-    // Global loads run one full iteration ahead of their use.  The loop is
-    // unrolled over the two LDS stages so that stage offsets are immediates.
+    // Ping-pong schedule.  Every block takes two barrier-separated phases per
+    // wave: an MFMA phase (S = K(j) Q^T and O += V(j-1)^T P(j-1)) and a VALU
+    // phase (softmax of block j).  The two waves of a query group share a SIMD
+    // and run one phase apart, so one wave's MFMAs overlap the other's
+    // softmax.  K stages hold K(j), K(j+1); V stages V(j-1), V(j).  Global
+    // loads are two phases ahead of their LDS store.
     TileMap<G> tm;
     tile_map<DT, D, BLK>(tm, a, tid);
     u32x4 kst[G::NKC];
     u32x4 vst[G::NKC];
     auto list_at = [&](int i) { return SPARSE ? __builtin_amdgcn_readfirstlane((int)list[i]) : i; };
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)a.k, 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)a.v, 0, -1, 0x00020000);
+    constexpr int KBASE = 0, VBASE = G::STAGES * G::TILEB;
+    const int lag = G::STAGES == 2 ? ks : 0;
+    const bool diag_last = list_at(n - 1) == I;            // the diagonal block, if kept, is the last
+    BlockOffs<G> off_v;                                    // offsets of the next V block to fetch
     {
-        const int J0 = list_at(0);
-        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, tm, b, g, J0);
-        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, tm, b, g, J0);
-        store_tile<DT, D, BLK>(kst, smem, tm);
-        store_tile<DT, D, BLK>(vst, smem + G::TILEB, tm);
-        const int J1 = n > 1 ? list_at(1) : J0;
-        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, tm, b, g, J1);
-        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, tm, b, g, J1);
+        const BlockOffs<G> off0 = block_offs<DT, D, BLK, PAGED>(a, tm, b, g, list_at(0));
+        load_tile<DT, D, BLK>(kst, krs, off0, tm);
+        store_tile<DT, D, BLK>(kst, smem + KBASE, tm);
+        const BlockOffs<G> off1 = n > 1 ? block_offs<DT, D, BLK, PAGED>(a, tm, b, g, list_at(1)) : off0;
+        load_tile<DT, D, BLK>(kst, krs, off1, tm);
+        load_tile<DT, D, BLK>(vst, vrs, off0, tm);
+        off_v = off1;
     }
     __syncthreads();
 
-    auto body = [&](auto stage, int it) {
-        constexpr int CUR = decltype(stage)::value;
-        constexpr int NXT = G::STAGES == 2 ? 1 - CUR : 0;
-        const int J = list_at(it);
-        const int J2 = it + 2 < n ? list_at(it + 2) : J;   // the tail re-fetches its own block
-        const char *kl = smem + CUR * 2 * G::TILEB;
-        const char *vl = kl + G::TILEB;
+    f32x16 s[G::NTW];                                     // scores of the block awaiting softmax
+    PPack<DT, D, BLK> pk;                                 // P of the block awaiting PV
+    int pscale = 127;                                     // its E8M0 scale (FP8)
+    const int nph = 2 * n + 2;
 
-        f32x16 s[G::NTW];
+    auto phase = [&](auto R, int p) {
+        constexpr int r = decltype(R)::value;
+        constexpr int ST = G::STAGES == 2 ? (r >> 1) : 0;     // K stage of this phase's MFMA work
+        const int q = p - lag;
+        if (q >= 0) {
+            const int j = q >> 1;
+            if ((q & 1) == 0) {
+                // ---- MFMA phase: S = K(j) Q^T, O += V(j-1)^T P(j-1)
+                if (j < n) {
+                    const char *kl = smem + KBASE + ST * G::TILEB;
 #pragma unroll
-        for (int t = 0; t < G::NTW; ++t) s[t] = qk_tile<DT, D, BLK>(qf, kl, t0 + t, lane);
-        if (J == I) {                                     // causal mask inside the diagonal block
-#pragma unroll
-            for (int t = 0; t < G::NTW; ++t)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = keymap<DT>(t0 + t, 8 * (e >> 2) + 4 * g32 + (e & 3));
-                    if (key > qrow) s[t][e] = ninf;
+                    for (int t = 0; t < G::NTW; ++t) s[t] = qk_tile<DT, D, BLK>(qf, kl, t0 + t, lane);
                 }
-        }
-        // (NaN never arises: -inf - -inf is kept out of every expression below)
-        float mx = ninf;
+                if (j >= 1) {
+                    const char *vl = smem + VBASE + (G::STAGES == 2 ? 1 - ST : 0) * G::TILEB;
+                    pv_block<DT, D, BLK>(o, lacc, pk, vl, t0, lane, pscale);
+                }
+            } else if (j < n) {
+                // ---- VALU phase: online softmax of block j
+                if (diag_last && j == n - 1) {            // causal mask inside the diagonal block
 #pragma unroll
-        for (int t = 0; t < G::NTW; ++t)
+                    for (int t = 0; t < G::NTW; ++t)
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[t][e], s[t][e + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // lazy rescale: only when some row's max grew by more than THRESH
-        const bool grow = m == ninf ? mx != ninf : (mx - m) * c > G::THRESH;
-        if (__ballot(grow)) {
-            const float m_new = fmaxf(m, mx);
-            const float alpha = m == ninf ? (m_new == ninf ? 1.0f : 0.0f) : __builtin_amdgcn_exp2f((m - m_new) * c);
-            m = m_new;
-            l *= alpha;
-            if constexpr (DT == kFP8) {
+                        for (int e = 0; e < 16; ++e) {
+                            const int key = keymap<DT>(t0 + t, 8 * (e >> 2) + 4 * g32 + (e & 3));
+                            if (key > qrow) s[t][e] = ninf;
+                        }
+                }
+                // (NaN never arises: -inf - -inf is kept out of every expression below)
+                float mx = ninf;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) lacc[e] *= alpha;
+                for (int t = 0; t < G::NTW; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[t][e], s[t][e + 1]));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                // lazy rescale: only when some row's max grew by more than THRESH
+                const bool grow = m == ninf ? mx != ninf : (mx - m) * c > G::THRESH;
+                if (__ballot(grow)) {
+                    const float m_new = fmaxf(m, mx);
+                    const float alpha =
+                        m == ninf ? (m_new == ninf ? 1.0f : 0.0f) : __builtin_amdgcn_exp2f((m - m_new) * c);
+                    m = m_new;
+                    l *= alpha;
+                    if constexpr (DT == kFP8) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) lacc[e] *= alpha;
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < G::NDT; ++dt)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+                }
+                // FP8: P of this block is cast as P * 2^e with e chosen per query so
+                // that the block's largest P lands in (128, 256]; the MFMA multiplies
+                // by the E8M0 scale 2^-e, so every block uses the full E4M3 range.
+                int e = 0;
+                if constexpr (DT == kFP8) {
+                    const float x = (mx == ninf || m == ninf) ? -1000.0f : (mx - m) * c;   // log2 of the largest P
+                    e = 8 - (int)ceilf(fmaxf(x, -92.0f));   // e in [0, 100]
+                }
+                const float mc = m == ninf ? 0.0f : m * c - (float)e;
+                float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};    // four partial sums: short add chains
+#pragma unroll
+                for (int t = 0; t < G::NTW; ++t)
+#pragma unroll
+                    for (int e2 = 0; e2 < 16; ++e2) {
+                        const float pe = __builtin_amdgcn_exp2f(fmaf(s[t][e2], c, -mc));
+                        s[t][e2] = pe;
+                        ls4[e2 & 3] += pe;
+                    }
+                const float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+                l += DT == kFP8 ? ldexpf(ls, -e) : ls;
+                pack_p<DT, D, BLK>(pk, s);
+                pscale = 127 - e;
             }
-#pragma unroll
-            for (int dt = 0; dt < G::NDT; ++dt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
         }
-        // FP8: P of this block is cast as P * 2^e with e chosen per query so that
-        // the block's largest P lands in (128, 256]; the MFMA multiplies by the
-        // E8M0 scale 2^-e, so every block uses the full E4M3 range.
-        int e = 0;
-        if constexpr (DT == kFP8) {
-            const float x = (mx == ninf || m == ninf) ? -1000.0f : (mx - m) * c;   // log2 of the largest P
-            e = 8 - (int)ceilf(fmaxf(x, -92.0f));           // e in [0, 100]
+        if constexpr ((r & 1) != 0) {
+            // ---- store K(jj+1) and V(jj), then fetch K(jj+2) and V(jj+1)
+            const int jj = (p - 1) >> 1;
+            const int last = n - 1;
+            const BlockOffs<G> off_k = block_offs<DT, D, BLK, PAGED>(a, tm, b, g, list_at(jj + 2 < last ? jj + 2 : last));
+            constexpr int KS = G::STAGES == 2 ? ((r >> 1) ^ 1) : 0;
+            constexpr int VS = G::STAGES == 2 ? (r >> 1) : 0;
+            if (jj + 1 < n) store_tile<DT, D, BLK>(kst, smem + KBASE + KS * G::TILEB, tm);
+            if (jj < n) store_tile<DT, D, BLK>(vst, smem + VBASE + VS * G::TILEB, tm);
+            load_tile<DT, D, BLK>(kst, krs, off_k, tm);
+            load_tile<DT, D, BLK>(vst, vrs, off_v, tm);
+            off_v = off_k;                                    // V(jj+2) is K(jj+2)'s block
         }
-        const float mc = m == ninf ? 0.0f : m * c - (float)e;
-        float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};            // four partial sums: short add chains
-#pragma unroll
-        for (int t = 0; t < G::NTW; ++t)
-#pragma unroll
-            for (int e2 = 0; e2 < 16; ++e2) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(s[t][e2], c, -mc));
-                s[t][e2] = pe;
-                ls4[e2 & 3] += pe;
-            }
-        const float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
-        l += DT == kFP8 ? ldexpf(ls, -e) : ls;
-        pv_block<DT, D, BLK>(o, lacc, s, vl, t0, lane, 127 - e);
-
-        const bool more = it + 1 < n;
-        if (more) {
-            if constexpr (G::STAGES == 1) __syncthreads();    // the only stage is free again
-            char *kn = smem + NXT * 2 * G::TILEB;
-            store_tile<DT, D, BLK>(kst, kn, tm);
-            store_tile<DT, D, BLK>(vst, kn + G::TILEB, tm);
-        }
-        load_tile<DT, D, BLK, PAGED>(kst, a.k, a, tm, b, g, J2);
-        load_tile<DT, D, BLK, PAGED>(vst, a.v, a, tm, b, g, J2);
-        if (more) __syncthreads();
+        __syncthreads();
     };
-    for (int it = 0; it < n; it += 2) {
-        body(std::integral_constant<int, 0>{}, it);
-        if (it + 1 < n) body(std::integral_constant<int, G::STAGES == 2 ? 1 : 0>{}, it + 1);
+    for (int p0 = 0; p0 < nph; p0 += 4) {
+        phase(std::integral_constant<int, 0>{}, p0);
+        if (p0 + 1 < nph) phase(std::integral_constant<int, 1>{}, p0 + 1);
+        if (p0 + 2 < nph) phase(std::integral_constant<int, 2>{}, p0 + 2);
+        if (p0 + 3 < nph) phase(std::integral_constant<int, 3>{}, p0 + 3);
     }
 
     // ---- merge the key parts, normalise, store --------------------------------
