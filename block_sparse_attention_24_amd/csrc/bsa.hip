@@ -73,6 +73,9 @@ struct Geo {
     // Lazy rescaling: the running max only moves when a block's max exceeds it
     // by more than THRESH (log2 units), so P stays below 2^THRESH.
     static constexpr float THRESH = 8.0f;
+    // FP8: normalise O by the MFMA-accumulated sum of the quantised P (an
+    // all-ones row of V^T) instead of the exact fp32 sum.
+    static constexpr bool QSUM = DT == kFP8;
     static_assert(BLK * KCH % NT == 0, "K chunks must divide over the threads");
 };
 
@@ -346,9 +349,11 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
                 }
                 o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pk.f8[t >> 1], o[dt], 0, 0, 0, 127, 0, pscale);
             }
-            const int one = 0x38383838;                   // four E4M3 1.0
-            const i32x8 ones = {one, one, one, one, one, one, one, one};
-            lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pk.f8[t >> 1], lacc, 0, 0, 0, 127, 0, pscale);
+            if constexpr (G::QSUM) {
+                const int one = 0x38383838;               // four E4M3 1.0
+                const i32x8 ones = {one, one, one, one, one, one, one, one};
+                lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pk.f8[t >> 1], lacc, 0, 0, 0, 127, 0, pscale);
+            }
         }
     } else {
 #pragma unroll
@@ -365,6 +370,69 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[D / 32], f32x16 &lacc, cons
             }
         }
     }
+}
+
+// FP8 MFMA phase in one piece: S = K(j) Q^T for this wave's two 32-key tiles
+// and O += V(j-1)^T P(j-1).  It runs unconditionally (at the edges of the loop
+// the extra products are discarded or add zeros), so it is one scheduling
+// region, and its order is pinned: LDS operands are fetched ahead of the MFMAs
+// that consume them, so the matrix core does not wait on LDS round trips.
+template <int D, int BLK>
+__device__ __forceinline__ void mfma_phase_fp8(f32x16 (&s)[2], f32x16 (&o)[D / 32], f32x16 &lacc,
+                                               const QFrag<kFP8, D> &qf,
+                                               const PPack<kFP8, D, BLK> &pk, int pscale, const char *kl,
+                                               const char *vl, int t0, int lane) {
+    using G = Geo<kFP8, D, BLK>;
+    static_assert(G::NTW == 2 && D == 128, "one 64-key PV step per wave, four 32-d tiles");
+    const int r = lane & 31, g = lane >> 5;
+    const int i16 = lane & 15, dhalf = 16 * ((lane >> 4) & 1);
+    auto kop = [&](int t, int st) {
+        const int key = keymap<kFP8>(t0 + t, r);
+        const u32x4 a0 = *reinterpret_cast<const u32x4 *>(kl + k_off<G>(key, 4 * st + 2 * g));
+        const u32x4 a1 = *reinterpret_cast<const u32x4 *>(kl + k_off<G>(key, 4 * st + 2 * g + 1));
+        return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    };
+    auto qop = [&](int st) {
+        const u32x4 b0 = qf.u[2 * st], b1 = qf.u[2 * st + 1];
+        return i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    };
+    const int kb = 64 * (t0 >> 1) + 32 * g;
+    auto vop = [&](int dt) {
+        const int ch = (32 * dt + dhalf) / 16, off = 8 * (i16 & 1);
+        i32x8 av;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const i32x2 x = lds_tr8(vl + k_off<G>(kb + 8 * q + (i16 >> 1), ch) + off);
+            av[2 * q] = x[0];
+            av[2 * q + 1] = x[1];
+        }
+        return av;
+    };
+    const i32x8 k00 = kop(0, 0), k01 = kop(0, 1), k10 = kop(1, 0), k11 = kop(1, 1);
+    const i32x8 v0 = vop(0);
+    f32x16 a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k00, qop(0), f32x16{}, 0, 0, 0, 0, 0, 0);
+    s[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k01, qop(1), a0, 0, 0, 0, 0, 0, 0);
+    const i32x8 v1 = vop(1);
+    f32x16 a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k10, qop(0), f32x16{}, 0, 0, 0, 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k11, qop(1), a1, 0, 0, 0, 0, 0, 0);
+    const i32x8 v2 = vop(2);
+    o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v0, pk.f8[0], o[0], 0, 0, 0, 127, 0, pscale);
+    const i32x8 v3 = vop(3);
+    o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v1, pk.f8[0], o[1], 0, 0, 0, 127, 0, pscale);
+    o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v2, pk.f8[0], o[2], 0, 0, 0, 127, 0, pscale);
+    o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v3, pk.f8[0], o[3], 0, 0, 0, 127, 0, pscale);
+    const int one = 0x38383838;                            // four E4M3 1.0: the sum of the quantised P
+    const i32x8 ones = {one, one, one, one, one, one, one, one};
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pk.f8[0], lacc, 0, 0, 0, 127, 0, pscale);
+    // issue order: 8 K reads + 4 V reads, 2 MFMA, 4 V reads, 2 MFMA, 4 V reads, 1 MFMA, 4 V reads, 4 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 template <int DT, int D, int BLK, bool SPARSE, bool PAGED>
@@ -480,29 +548,46 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
         load_tile<DT, D, BLK>(vst, vrs, off0, tm);
         off_v = off1;
     }
+    if constexpr (DT == kFP8) {
+        // the first MFMA phase multiplies this V stage by P = 0: it must hold no NaN
+        u32x4 *vz = reinterpret_cast<u32x4 *>(smem + VBASE + (G::STAGES == 2 ? 1 : 0) * G::TILEB);
+        for (int i = tid; i < G::TILEB / 16; i += G::NT) vz[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     __syncthreads();
 
     f32x16 s[G::NTW];                                     // scores of the block awaiting softmax
-    PPack<DT, D, BLK> pk;                                 // P of the block awaiting PV
+    PPack<DT, D, BLK> pk = {};                            // P of the block awaiting PV (zero before the first)
     int pscale = 127;                                     // its E8M0 scale (FP8)
     const int nph = 2 * n + 2;
 
     auto phase = [&](auto R, int p) {
         constexpr int r = decltype(R)::value;
         constexpr int ST = G::STAGES == 2 ? (r >> 1) : 0;     // K stage of this phase's MFMA work
+        // odd phases fetch K(jj+2): look its rows up first, so the list read and
+        // the page-table loads overlap this phase's work
+        const int jj = (p - 1) >> 1;
+        BlockOffs<G> off_k;
+        if constexpr ((r & 1) != 0) {
+            const int last = n - 1;
+            off_k = block_offs<DT, D, BLK, PAGED>(a, tm, b, g, list_at(jj + 2 < last ? jj + 2 : last));
+        }
         const int q = p - lag;
         if (q >= 0) {
             const int j = q >> 1;
             if ((q & 1) == 0) {
                 // ---- MFMA phase: S = K(j) Q^T, O += V(j-1)^T P(j-1)
-                if (j < n) {
-                    const char *kl = smem + KBASE + ST * G::TILEB;
+                const char *kl = smem + KBASE + ST * G::TILEB;
+                const char *vl = smem + VBASE + (G::STAGES == 2 ? 1 - ST : 0) * G::TILEB;
+                if constexpr (DT == kFP8 && G::NTW == 2 && D == 128) {
+                    // unconditional: at j == n the scores are never used; at j == 0 P and
+                    // the V stage read are zero (cleared before the loop)
+                    mfma_phase_fp8<D, BLK>(s, o, lacc, qf, pk, pscale, kl, vl, t0, lane);
+                } else {
+                    if (j < n) {
 #pragma unroll
-                    for (int t = 0; t < G::NTW; ++t) s[t] = qk_tile<DT, D, BLK>(qf, kl, t0 + t, lane);
-                }
-                if (j >= 1) {
-                    const char *vl = smem + VBASE + (G::STAGES == 2 ? 1 - ST : 0) * G::TILEB;
-                    pv_block<DT, D, BLK>(o, lacc, pk, vl, t0, lane, pscale);
+                        for (int t = 0; t < G::NTW; ++t) s[t] = qk_tile<DT, D, BLK>(qf, kl, t0 + t, lane);
+                    }
+                    if (j >= 1) pv_block<DT, D, BLK>(o, lacc, pk, vl, t0, lane, pscale);
                 }
             } else if (j < n) {
                 // ---- VALU phase: online softmax of block j
@@ -516,12 +601,18 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
                         }
                 }
                 // (NaN never arises: -inf - -inf is kept out of every expression below)
-                float mx = ninf;
+                // block max of this lane's scores as a balanced tree, then across lane ^ 32
+                float mt[G::NTW * 4];
 #pragma unroll
                 for (int t = 0; t < G::NTW; ++t)
 #pragma unroll
-                    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[t][e], s[t][e + 1]));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    for (int e = 0; e < 4; ++e)
+                        mt[4 * t + e] = fmaxf(fmaxf(s[t][4 * e], s[t][4 * e + 1]), fmaxf(s[t][4 * e + 2], s[t][4 * e + 3]));
+#pragma unroll
+                for (int w = G::NTW * 4; w > 1; w >>= 1)
+#pragma unroll
+                    for (int e = 0; e < w / 2; ++e) mt[e] = fmaxf(mt[e], mt[e + w / 2]);
+                const float mx = max_xor32(mt[0]);
                 // lazy rescale: only when some row's max grew by more than THRESH
                 const bool grow = m == ninf ? mx != ninf : (mx - m) * c > G::THRESH;
                 if (__ballot(grow)) {
@@ -530,7 +621,7 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
                         m == ninf ? (m_new == ninf ? 1.0f : 0.0f) : __builtin_amdgcn_exp2f((m - m_new) * c);
                     m = m_new;
                     l *= alpha;
-                    if constexpr (DT == kFP8) {
+                    if constexpr (DT == kFP8 && G::QSUM) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e) lacc[e] *= alpha;
                     }
@@ -565,9 +656,6 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
         }
         if constexpr ((r & 1) != 0) {
             // ---- store K(jj+1) and V(jj), then fetch K(jj+2) and V(jj+1)
-            const int jj = (p - 1) >> 1;
-            const int last = n - 1;
-            const BlockOffs<G> off_k = block_offs<DT, D, BLK, PAGED>(a, tm, b, g, list_at(jj + 2 < last ? jj + 2 : last));
             constexpr int KS = G::STAGES == 2 ? ((r >> 1) ^ 1) : 0;
             constexpr int VS = G::STAGES == 2 ? (r >> 1) : 0;
             if (jj + 1 < n) store_tile<DT, D, BLK>(kst, smem + KBASE + KS * G::TILEB, tm);
@@ -586,8 +674,8 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
     }
 
     // ---- merge the key parts, normalise, store --------------------------------
-    l += __shfl_xor(l, 32);                                // exact sum of P: the LSE
-    float lq = DT == kFP8 ? lacc[0] : l;                   // sum of the P that multiplied V
+    l = sum_xor32(l);                                      // exact sum of P: the LSE
+    float lq = DT == kFP8 && G::QSUM ? lacc[0] : l;        // the sum O is normalised by
     if constexpr (G::KSPLIT == 2) {
         __syncthreads();                                  // stages are free: reuse for partial O
         float *po = reinterpret_cast<float *>(smem) + wq * 64 * (D / 2);
