@@ -435,6 +435,60 @@ __device__ __forceinline__ void mfma_phase_fp8(f32x16 (&s)[2], f32x16 (&o)[D / 3
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
+// Kept blocks J <= I of row (b, h, I), in ascending order, into list[];
+// returns their count.  Every thread of the workgroup calls it (two barriers).
+template <int NW, bool SPARSE>
+__device__ __forceinline__ int build_block_list(const BsaArgs &a, int b, int h, int I, uint16_t *list,
+                                                int *wave_sum, int tid, int lane, int wave) {
+    if constexpr (!SPARSE) {
+        return I + 1;
+    } else {
+        const int nw = (I >> 5) + 1;                          // words holding J <= I
+        uint32_t w = 0;
+        if (tid < nw) {
+            w = a.mask[(((size_t)b * a.hq + h) * a.nb + I) * a.words + tid];
+            if (tid == nw - 1 && (I & 31) != 31) w &= (2u << (I & 31)) - 1u;
+        }
+        const int cnt = __popc(w);
+        int incl = cnt;                                       // inclusive scan in the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        if (lane == 63) wave_sum[wave] = incl;
+        __syncthreads();
+        int base = 0, n = 0;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            base += k < wave ? wave_sum[k] : 0;
+            n += wave_sum[k];
+        }
+        int pos = base + incl - cnt;
+        while (w) {
+            const int bit = __builtin_ctz(w);
+            list[pos++] = (uint16_t)(32 * tid + bit);
+            w &= w - 1;
+        }
+        __syncthreads();
+        return n;
+    }
+}
+
+// Output of a query row that sees no key: O = 0, LSE = -inf.  Lanes l and
+// l ^ 32 of the calling wave share the row and write alternate elements.
+template <int DT, int D>
+__device__ __forceinline__ void write_empty_row(const BsaArgs &a, int b, int h, int token, int g32) {
+    if constexpr (DT == kF32) {
+        float *op = reinterpret_cast<float *>(a.o) + (((size_t)b * a.seq + token) * a.hq + h) * D;
+        for (int d = g32; d < D; d += 2) op[d] = 0.0f;
+    } else {
+        uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + (((size_t)b * a.seq + token) * a.hq + h) * D;
+        for (int d = g32; d < D; d += 2) op[d] = 0;
+    }
+    if (a.lse && g32 == 0) a.lse[((size_t)b * a.hq + h) * a.seq + token] = -__builtin_huge_valf();
+}
+
 template <int DT, int D, int BLK, bool SPARSE, bool PAGED>
 __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a) {
     using G = Geo<DT, D, BLK>;
@@ -458,55 +512,12 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
     const int h = (a.hq % 8 == 0) ? (j % 8) * (a.hq / 8) + j / 8 : j;
     const int g = h / (a.hq / a.hkv);
 
-    // ---- kept-block list, built once before the loop -------------------------
-    int n;
-    if constexpr (SPARSE) {
-        const int nw = (I >> 5) + 1;                          // words holding J <= I
-        uint32_t w = 0;
-        if (tid < nw) {
-            w = a.mask[(((size_t)b * a.hq + h) * a.nb + I) * a.words + tid];
-            if (tid == nw - 1 && (I & 31) != 31) w &= (2u << (I & 31)) - 1u;
-        }
-        const int cnt = __popc(w);
-        int incl = cnt;                                       // inclusive scan in the wave
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off);
-            if (lane >= off) incl += y;
-        }
-        if (lane == 63) wave_sum[wave] = incl;
-        __syncthreads();
-        int base = 0;
-        n = 0;
-#pragma unroll
-        for (int k = 0; k < G::NW; ++k) {
-            base += k < wave ? wave_sum[k] : 0;
-            n += wave_sum[k];
-        }
-        int pos = base + incl - cnt;
-        while (w) {
-            const int bit = __builtin_ctz(w);
-            list[pos++] = (uint16_t)(32 * tid + bit);
-            w &= w - 1;
-        }
-        __syncthreads();
-    } else {
-        n = I + 1;
-    }
+    const int n = build_block_list<G::NW, SPARSE>(a, b, h, I, list, wave_sum, tid, lane, wave);
 
     const int qrow = 32 * wq + (lane & 31);               // query row in the block
     const int token = I * BLK + qrow;
     if (n == 0) {                                         // nothing visible: O = 0, LSE = -inf
-        if (ks == 0) {
-            if constexpr (DT == kF32) {
-                float *op = reinterpret_cast<float *>(a.o) + (((size_t)b * a.seq + token) * a.hq + h) * D;
-                for (int d = g32; d < D; d += 2) op[d] = 0.0f;
-            } else {
-                uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + (((size_t)b * a.seq + token) * a.hq + h) * D;
-                for (int d = g32; d < D; d += 2) op[d] = 0;
-            }
-            if (a.lse && g32 == 0) a.lse[((size_t)b * a.hq + h) * a.seq + token] = -__builtin_huge_valf();
-        }
+        if (ks == 0) write_empty_row<DT, D>(a, b, h, token, g32);
         return;
     }
 
@@ -727,15 +738,413 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
             l > 0.0f ? fmaf(m, a.tau_eff, logf(l)) : ninf;
 }
 
+// ---------------------------------------------------------------------------
+// FP8, d = 128, 128-token blocks: a software-pipelined kernel.
+//
+// One wave issues a VALU instruction only every few cycles, while the two
+// waves of a SIMD together reach about twice that rate, and a wave keeps
+// issuing independent VALU work while its own MFMAs run.  So all eight waves
+// run one pipeline: while a wave computes the softmax of block j it also
+// issues the MFMAs of S = K(j+1) Q^T (under the row max) and of
+// O += V(j-1)^T P(j-1) (under the exponentials).  K and V move from global
+// memory straight into LDS (buffer loads that write LDS, no staging
+// registers), three blocks ahead of use, through four LDS stages each, with
+// one barrier per block.  Both waves of a SIMD are in the softmax at the same
+// time, so its VALU issues at the two-wave rate while the MFMAs of both fill
+// the matrix core.
+//
+// When the running max moves, O and the MFMA row sums are rescaled at the
+// start of the next block, after the PV MFMA of the old scale has been added,
+// so that the rescale needs no branch inside the scheduling region.
+namespace fp8p {
+constexpr int D = 128, BLK = 128, NT = 512, NW = 8;
+constexpr int NST = 4;                           // LDS stages of K and of V
+constexpr int TILE = BLK * D;                    // bytes of one K or V block
+constexpr int KST = 0, VST = NST * TILE;         // K stages, then V stages
+constexpr int LIST_OFF = 2 * NST * TILE;         // kept-block list (u16) after the stages
+constexpr int LIST = 4096;
+constexpr int WSUM_OFF = LIST_OFF + 2 * LIST;    // per-wave counts of the list scan
+constexpr int ML_OFF = WSUM_OFF + 4 * NW;        // (M, l, lq) of the second key half
+constexpr int SMEM = ML_OFF + 3 * 4 * 64 * 4;
+constexpr int VM_ITER = 4;                       // loads into LDS per wave and iteration
+constexpr float THRESH = 8.0f;                   // lazy rescale: P stays below 2^THRESH
+constexpr float M_NONE = -3.0e38f;               // running max before any finite score
+
+// 16-byte chunk swizzles of a K and a V row (key = row within the block).
+// K: the 8 rows of equal parity that a 16-lane group reads for S = K Q^T
+// ({0..7, 32..39} plus a multiple of 16) get 8 distinct chunks, and key + 16
+// keeps the pattern, so the second key tile is an immediate offset.  V: the 4
+// rows of equal parity under one transposing read get distinct chunk pairs,
+// and key + 8 keeps the pattern.
+__device__ __forceinline__ int swz_k(int key) { return ((key >> 1) & 3) | (((key >> 5) & 1) << 2); }
+__device__ __forceinline__ int swz_v(int key) { return ((key >> 1) & 3) << 1; }
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0), then the workgroup barrier.  The barrier
+// itself waits for nothing, so the last VM loads into LDS stay in flight
+// across it.
+template <int VM>
+__device__ __forceinline__ void sync_vm() {
+    static_assert(VM < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of a whole tensor (smaller than 4 GiB: checked on the host).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *p) {
+    const unsigned long long a = (unsigned long long)p;
+    return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), -1, 0x00020000};
+}
+
+// 16 bytes per lane from global memory (descriptor + soff + voff) straight
+// into LDS at byte m0 + 16 * lane.  Written as asm so that the compiler, which
+// would otherwise make every later transposing LDS read wait for all such loads,
+// leaves the pacing to the explicit vmcnt waits; the asm has no outputs.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned m0, unsigned voff, unsigned soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+}  // namespace fp8p
+
+template <bool SPARSE, bool PAGED>
+__global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
+    using namespace fp8p;
+    // One LDS object: the compiler then leaves LDS reads that follow a load
+    // into LDS unordered with it, and the explicit waits and barriers below
+    // order them.
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+    uint16_t *list = reinterpret_cast<uint16_t *>(smem + LIST_OFF);
+    int *wave_sum = reinterpret_cast<int *>(smem + WSUM_OFF);
+    float *part_ml = reinterpret_cast<float *>(smem + ML_OFF);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g32 = lane >> 5, r32 = lane & 31;
+    const int wq = wave & 3;                               // query group: rows 32 wq .. 32 wq + 31
+    const int ks = wave >> 2;                              // key half: keys 64 ks .. 64 ks + 63 of each block
+
+    // heaviest query blocks first; the heads of one KV group on one XCD
+    const int wg = blockIdx.x;
+    const int qidx = wg / a.hq, jh = wg % a.hq;
+    const int I = a.nb - 1 - qidx / a.batch;
+    const int b = qidx % a.batch;
+    const int h = (a.hq % 8 == 0) ? (jh % 8) * (a.hq / 8) + jh / 8 : jh;
+    const int g = h / (a.hq / a.hkv);
+
+    const int qrow = 32 * wq + r32;
+    const int token = I * BLK + qrow;
+    QFrag<kFP8, D> qf;                                     // in flight while the list is built
+    load_q<kFP8, D>(qf, a.q + (((size_t)b * a.seq + token) * a.hq + h) * (size_t)D, g32);
+    const int n = build_block_list<NW, SPARSE>(a, b, h, I, list, wave_sum, tid, lane, wave);
+    if (n == 0) {
+        if (ks == 0) write_empty_row<kFP8, D>(a, b, h, token, g32);
+        return;
+    }
+    // Q has landed before the first load into LDS: the compiler does not count
+    // those loads, so a wait for Q after them would drain them too.
+    asm volatile("" :: "v"(qf.u[0]), "v"(qf.u[1]), "v"(qf.u[2]), "v"(qf.u[3]));
+
+    // Loop-invariant LDS offsets.  K operand of S = K Q^T: row kkey of a K
+    // stage (+16 rows for the second tile), d chunk 4 st + 2 g32 + hh.  V^T
+    // operand: rows vrow + 8 q of a V stage, d chunk 2 dt + ((lane >> 4) & 1),
+    // byte half lane & 1.
+    const int kkey = 64 * ks + 32 * ((r32 >> 2) & 1) + 4 * (r32 >> 3) + (r32 & 3);
+    int koff[4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            koff[2 * st + hh] = KST + kkey * D + (((4 * st + 2 * g32 + hh) ^ swz_k(kkey)) << 4);
+    const int vrow = 64 * ks + 32 * g32 + ((lane & 15) >> 1);
+    int voff[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+        voff[dt] = VST + vrow * D + (((2 * dt + ((lane >> 4) & 1)) ^ swz_v(vrow)) << 4) + 8 * (lane & 1);
+
+    // Global -> LDS: wave w moves rows 16 w + 8 i + (lane >> 3) of a block into
+    // LDS chunk lane & 7 of the row (i = 0, 1); its 16 rows lie in one page.
+    const unsigned row_bytes = (unsigned)a.hkv * D;
+    int dk[2], dv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * wave + 8 * i + (lane >> 3), cl = lane & 7;
+        dk[i] = (8 * i + (lane >> 3)) * (int)row_bytes + ((cl ^ swz_k(row)) << 4);
+        dv[i] = (8 * i + (lane >> 3)) * (int)row_bytes + ((cl ^ swz_v(row)) << 4);
+    }
+    auto list_at = [&](int i) { return SPARSE ? __builtin_amdgcn_readfirstlane((int)list[i]) : i; };
+    // The block table is read-only here: reading it through the constant
+    // address space makes the lookups scalar loads, off the vector memory
+    // counter that paces the loads into LDS.
+    const_i32 *table = (const_i32 *)a.table;
+    auto src_off = [&](int J) -> unsigned {              // byte offset of this wave's first row of block J
+        const int tok = J * BLK + 16 * wave;
+        unsigned row;
+        if constexpr (PAGED) {
+            const int page = table[b * a.pages_per_seq + (tok >> a.page_log2)];
+            row = ((unsigned)page << a.page_log2) | (unsigned)(tok & ((1 << a.page_log2) - 1));
+        } else {
+            row = (unsigned)(b * a.seq + tok);
+        }
+        return row * row_bytes + (unsigned)g * D;
+    };
+    const i32x4 krs = buffer_rsrc(a.k), vrs = buffer_rsrc(a.v);
+    const unsigned lds_wave = (unsigned)(size_t)(lds_char *)smem + 16 * wave * D;   // this wave's rows in a stage
+    auto dma = [&](i32x4 rs, int stage_off, unsigned so, const int (&vo)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) load_lds16(rs, lds_wave + stage_off + 8 * i * D, (unsigned)vo[i], so);
+    };
+
+    auto qop = [&](int st) {
+        const u32x4 b0 = qf.u[2 * st], b1 = qf.u[2 * st + 1];
+        return i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    };
+    // K operand of tile t, d step st, from the K stage at byte offset ko
+    auto kop = [&](int ko, int t, int st) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4 *>(smem + ko + koff[2 * st] + t * 16 * D);
+        const u32x4 a1 = *reinterpret_cast<const u32x4 *>(smem + ko + koff[2 * st + 1] + t * 16 * D);
+        return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    };
+    // V^T operand of d tile dt from the V stage at byte offset vo (from VST)
+    auto vop = [&](int vo, int dt) {
+        i32x8 av;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const i32x2 x = lds_tr8(smem + vo + voff[dt] + q * 8 * D);
+            av[2 * q] = x[0];
+            av[2 * q + 1] = x[1];
+        }
+        return av;
+    };
+    auto mfma8 = [](const i32x8 &x, const i32x8 &y, const f32x16 &acc, int sy) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, 0, 0, 0, 127, 0, sy);
+    };
+    const int one = 0x38383838;                            // four E4M3 1.0
+    const i32x8 ones = {one, one, one, one, one, one, one, one};
+
+    const float c = a.c_exp2;
+    const float ninf = -__builtin_huge_valf();
+    f32x16 o[4] = {};
+    f32x16 lacc = {};                                      // sum of the quantised P, by MFMA (all-ones row)
+    float M = M_NONE, Mthr = M_NONE;                       // running max (log2 units) and M + THRESH
+    float l = 0.0f;                                        // this lane's exact sum of P (relative to 2^M)
+    f32x16 s[2];                                           // scores of the block awaiting softmax
+    i32x8 pk = {};                                         // P of the block awaiting PV, E4M3
+    int psc = 127;                                         // its E8M0 scale
+    const bool diag_last = list_at(n - 1) == I;            // the diagonal block, if kept, is the last
+
+    // ---- prologue --------------------------------------------------------------
+    // As if iterations -3 .. -1 had run: K(0..3) and V(0..1) loading, V(-1)
+    // standing in V stage 3 (a copy of V(0): the first PV multiplies it by
+    // P = 0, so it only has to be finite, which V(0) is wherever O is).
+    {
+        const int last = n - 1;
+        const unsigned s0 = src_off(list_at(0));
+        const unsigned s1 = src_off(list_at(min(1, last)));
+        dma(krs, KST, s0, dk);
+        dma(krs, KST + TILE, s1, dk);
+        dma(vrs, VST + 3 * TILE, s0, dv);
+        dma(krs, KST + 2 * TILE, src_off(list_at(min(2, last))), dk);
+        dma(vrs, VST, s0, dv);
+        dma(krs, KST + 3 * TILE, src_off(list_at(min(3, last))), dk);
+        dma(vrs, VST + TILE, s1, dv);
+    }
+    unsigned so_k = src_off(list_at(min(4, n - 1)));      // K(j+4) of the next iteration
+    unsigned so_v = src_off(list_at(min(2, n - 1)));      // V(j+2) of the next iteration
+    sync_vm<3 * VM_ITER>();                                // K(0) has landed
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s[t] = mfma8(kop(KST, t, 1), qop(1), mfma8(kop(KST, t, 0), qop(0), f32x16{}, 127), 127);
+
+    // ---- main loop: iteration j = softmax(j) with QK(j+1) and PV(j-1) ---------
+    // Stages (R = j mod 4): K(j+1) is read from K stage R+1 while K(j+4) loads
+    // into K stage R; V(j-1) is read from V stage R+3 while V(j+2) loads into V
+    // stage R+2.  Every iteration issues VM_ITER loads per wave, so "all but the
+    // last 2 VM_ITER" are the loads of iteration j-3.
+    float alpha = 1.0f;                                    // rescale of O and lacc still to apply
+    auto rescale_o = [&]() {
+        // O holds the PV MFMAs up to block j-2 at the scale of M before block
+        // j-1 moved it; bring it (and lacc) to the current scale before PV(j-1).
+        if (__ballot(alpha != 1.0f)) {
+            asm volatile("");                              // (a real branch: taken a few times per row)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) lacc[e] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        }
+    };
+    auto iter = [&](auto RR, int j) {
+        constexpr int R = decltype(RR)::value;
+        constexpr int KRD = KST + ((R + 1) % NST) * TILE, VRD = ((R + 3) % NST) * TILE;
+        sync_vm<2 * VM_ITER>();                            // K(j+1), V(j-1) have landed; stages R, R+2 are free
+        dma(krs, KST + R * TILE, so_k, dk);                // K(j+4)
+        dma(vrs, VST + ((R + 2) % NST) * TILE, so_v, dv);  // V(j+2)
+        so_k = src_off(list_at(min(j + 5, n - 1)));
+        so_v = src_off(list_at(min(j + 3, n - 1)));
+        rescale_o();
+        if (diag_last && j == n - 1) {                     // causal mask inside the diagonal block
+            asm volatile("");                              // (a real branch: taken once per row)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (keymap<kFP8>(2 * ks + t, 8 * (e >> 2) + 4 * g32 + (e & 3)) > qrow) s[t][e] = ninf;
+        }
+        // ---- one scheduling region: S(j+1) = K(j+1) Q^T under the row max of
+        // S(j), O += V(j-1)^T P(j-1) under the exponentials of block j
+        const i32x8 k00 = kop(KRD, 0, 0), k01 = kop(KRD, 0, 1), k10 = kop(KRD, 1, 0), k11 = kop(KRD, 1, 1);
+        f32x16 sn0 = mfma8(k00, qop(0), f32x16{}, 127);
+        f32x16 sn1 = mfma8(k10, qop(0), f32x16{}, 127);
+        sn0 = mfma8(k01, qop(1), sn0, 127);
+        sn1 = mfma8(k11, qop(1), sn1, 127);
+        float mt[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                mt[4 * t + e] = fmaxf(fmaxf(s[t][4 * e], s[t][4 * e + 1]), fmaxf(s[t][4 * e + 2], s[t][4 * e + 3]));
+        const float mx = max_xor32(fmaxf(fmaxf(fmaxf(mt[0], mt[1]), fmaxf(mt[2], mt[3])),
+                                         fmaxf(fmaxf(mt[4], mt[5]), fmaxf(mt[6], mt[7]))));
+        const float xm = mx * c;                           // the block's row max in log2 units
+        const float Mn = xm > Mthr ? xm : M;               // lazy: move only past M + THRESH
+        alpha = __builtin_amdgcn_exp2f(M - Mn);            // 1 unless the max moved
+        M = Mn;
+        Mthr = Mn + THRESH;
+        // P is cast as P * 2^e, e = 8 - ce, so that the block's largest P lands in
+        // (128, 256]; the PV MFMA multiplies by 2^-e through the E8M0 scale 127 - e.
+        const float ce = ceilf(fmaxf(xm - M, -92.0f));     // xm - M <= THRESH, so e >= 0
+        const float mc = (M - 8.0f) + ce;
+        const i32x8 v0 = vop(VRD, 0), v1 = vop(VRD, 1);
+        o[0] = mfma8(v0, pk, o[0], psc);
+        const i32x8 v2 = vop(VRD, 2);
+        o[1] = mfma8(v1, pk, o[1], psc);
+        const i32x8 v3 = vop(VRD, 3);
+        o[2] = mfma8(v2, pk, o[2], psc);
+        o[3] = mfma8(v3, pk, o[3], psc);
+        lacc = mfma8(ones, pk, lacc, psc);
+        float ls[4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(s[t][e], c, -mc));
+                s[t][e] = pe;
+                ls[e & 3] = (t == 0 && e < 4) ? pe : ls[e & 3] + pe;
+            }
+        const int ice = (int)ce;
+        l = fmaf(l, alpha, ldexpf((ls[0] + ls[1]) + (ls[2] + ls[3]), ice - 8));
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const f32x16 &src = s[w >> 2];
+            const int ee = 4 * (w & 3);
+            const int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], __float_as_int(src[ee]), false);
+            pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
+        }
+        psc = 119 + ice;
+        s[0] = sn0;
+        s[1] = sn1;
+        // issue order: K reads, QK MFMAs spaced out by the max tree, V reads, PV
+        // MFMAs spaced out by the exponentials
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    };
+    for (int j = 0; j < n; j += NST) {
+        iter(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < n) iter(std::integral_constant<int, 1>{}, j + 1);
+        if (j + 2 < n) iter(std::integral_constant<int, 2>{}, j + 2);
+        if (j + 3 < n) iter(std::integral_constant<int, 3>{}, j + 3);
+    }
+    sync_vm<2 * VM_ITER>();                                // V(n-1) has landed
+    rescale_o();
+    {
+        const int vo = ((n - 1) % NST) * TILE;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] = mfma8(vop(vo, dt), pk, o[dt], psc);
+        lacc = mfma8(ones, pk, lacc, psc);
+    }
+
+    // ---- merge the key halves, normalise, store -------------------------------
+    l = sum_xor32(l);                                      // exact sum of P: the LSE
+    float lq = lacc[0];                                    // sum of the quantised P: O's denominator
+    sync_vm<0>();                                          // every load into LDS is done: stages are free
+    float *po = reinterpret_cast<float *>(smem) + wq * 64 * (D / 2);
+    if (ks == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) po[(dt * 16 + e) * 64 + lane] = o[dt][e];
+        part_ml[(3 * wq) * 64 + lane] = M;
+        part_ml[(3 * wq + 1) * 64 + lane] = l;
+        part_ml[(3 * wq + 2) * 64 + lane] = lq;
+    }
+    __syncthreads();
+    if (ks == 1) return;
+    const float M1 = part_ml[(3 * wq) * 64 + lane];
+    const float l1 = part_ml[(3 * wq + 1) * 64 + lane];
+    const float lq1 = part_ml[(3 * wq + 2) * 64 + lane];
+    const float mm = fmaxf(M, M1);
+    const float a0 = __builtin_amdgcn_exp2f(M - mm), a1 = __builtin_amdgcn_exp2f(M1 - mm);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] = o[dt][e] * a0 + po[(dt * 16 + e) * 64 + lane] * a1;
+    l = l * a0 + l1 * a1;
+    lq = lq * a0 + lq1 * a1;
+    const float inv = lq > 0.0f ? a.o_scale / lq : 0.0f;
+    const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * dt + 8 * i + 4 * g32;
+            u32x2 u;
+            u.x = f32_to_bf16_bits(o[dt][4 * i] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 1] * inv) << 16);
+            u.y = f32_to_bf16_bits(o[dt][4 * i + 2] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 3] * inv) << 16);
+            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = u;
+        }
+    if (a.lse && g32 == 0)
+        a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
+}
+
 template <int DT, int D, int BLK>
 hipError_t launch_cfg(const BsaArgs &a, bool sparse, hipStream_t st) {
     using G = Geo<DT, D, BLK>;
     const dim3 grid((unsigned)(a.batch * a.hq * a.nb));
     const bool paged = a.table != nullptr;
-    if (sparse && paged) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, true, true>), grid, dim3(G::NT), 0, st, a);
-    else if (sparse) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, true, false>), grid, dim3(G::NT), 0, st, a);
-    else if (paged) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, false, true>), grid, dim3(G::NT), 0, st, a);
-    else hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, false, false>), grid, dim3(G::NT), 0, st, a);
+    if constexpr (DT == kFP8 && D == 128 && BLK == 128) {
+        if (sparse && paged) hipLaunchKernelGGL((bsa_fp8_kernel<true, true>), grid, dim3(fp8p::NT), 0, st, a);
+        else if (sparse) hipLaunchKernelGGL((bsa_fp8_kernel<true, false>), grid, dim3(fp8p::NT), 0, st, a);
+        else if (paged) hipLaunchKernelGGL((bsa_fp8_kernel<false, true>), grid, dim3(fp8p::NT), 0, st, a);
+        else hipLaunchKernelGGL((bsa_fp8_kernel<false, false>), grid, dim3(fp8p::NT), 0, st, a);
+    } else {
+        if (sparse && paged) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, true, true>), grid, dim3(G::NT), 0, st, a);
+        else if (sparse) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, true, false>), grid, dim3(G::NT), 0, st, a);
+        else if (paged) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, false, true>), grid, dim3(G::NT), 0, st, a);
+        else hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, false, false>), grid, dim3(G::NT), 0, st, a);
+    }
     return hipGetLastError();
 }
 
