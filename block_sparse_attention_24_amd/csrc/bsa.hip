@@ -879,17 +879,17 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     // address space makes the lookups scalar loads, off the vector memory
     // counter that paces the loads into LDS.
     const_i32 *table = (const_i32 *)a.table;
-    auto src_off = [&](int J) -> unsigned {              // byte offset of this wave's first row of block J
-        const int tok = J * BLK + 16 * wave;
+    // byte offset of this wave's first row of a block: its token, and its page when paged
+    auto page_of = [&](int tok) -> int { return PAGED ? table[b * a.pages_per_seq + (tok >> a.page_log2)] : 0; };
+    auto row_off = [&](int tok, int page) -> unsigned {
         unsigned row;
-        if constexpr (PAGED) {
-            const int page = table[b * a.pages_per_seq + (tok >> a.page_log2)];
-            row = ((unsigned)page << a.page_log2) | (unsigned)(tok & ((1 << a.page_log2) - 1));
-        } else {
-            row = (unsigned)(b * a.seq + tok);
-        }
+        if constexpr (PAGED) row = ((unsigned)page << a.page_log2) | (unsigned)(tok & ((1 << a.page_log2) - 1));
+        else row = (unsigned)(b * a.seq + tok);
         return row * row_bytes + (unsigned)g * D;
     };
+    auto tok_of = [&](int J) { return J * BLK + 16 * wave; };
+    auto src_off = [&](int J) -> unsigned { return row_off(tok_of(J), page_of(tok_of(J))); };
+    auto list_raw = [&](int i) -> int { return SPARSE ? (int)list[i] : i; };
     const i32x4 krs = buffer_rsrc(a.k), vrs = buffer_rsrc(a.v);
     const unsigned lds_wave = (unsigned)(size_t)(lds_char *)smem + 16 * wave * D;   // this wave's rows in a stage
     auto dma = [&](i32x4 rs, int stage_off, unsigned so, const int (&vo)[2]) {
@@ -939,8 +939,8 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     // As if iterations -3 .. -1 had run: K(0..3) and V(0..1) loading, V(-1)
     // standing in V stage 3 (a copy of V(0): the first PV multiplies it by
     // P = 0, so it only has to be finite, which V(0) is wherever O is).
+    const int last = n - 1;
     {
-        const int last = n - 1;
         const unsigned s0 = src_off(list_at(0));
         const unsigned s1 = src_off(list_at(min(1, last)));
         dma(krs, KST, s0, dk);
@@ -951,8 +951,14 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         dma(krs, KST + 3 * TILE, src_off(list_at(min(3, last))), dk);
         dma(vrs, VST + TILE, s1, dv);
     }
-    unsigned so_k = src_off(list_at(min(4, n - 1)));      // K(j+4) of the next iteration
-    unsigned so_v = src_off(list_at(min(2, n - 1)));      // V(j+2) of the next iteration
+    // Row lookups run ahead of the loads that use them, so that no wave waits
+    // on them: the list entry is read at the end of iteration i-3, the page
+    // table at the end of iteration i-2, the offset computed at the end of
+    // iteration i-1 for the loads of iteration i (K(i+4), V(i+2)).
+    unsigned so_k = src_off(list_at(min(4, last))), so_v = src_off(list_at(min(2, last)));   // iteration 0
+    int tk = tok_of(list_at(min(5, last))), tv = tok_of(list_at(min(3, last)));             // iteration 1
+    int pgk = page_of(tk), pgv = page_of(tv);
+    int lk = list_raw(min(6, last)), lv = list_raw(min(4, last));                          // iteration 2
     sync_vm<3 * VM_ITER>();                                // K(0) has landed
 #pragma unroll
     for (int t = 0; t < 2; ++t) s[t] = mfma8(kop(KST, t, 1), qop(1), mfma8(kop(KST, t, 0), qop(0), f32x16{}, 127), 127);
@@ -976,14 +982,24 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
                 for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
         }
     };
+    // Scores and P alternate between two register sets from one block to the
+    // next (the loop is unrolled by an even count), so nothing is copied.
+    f32x16 sB[2];
+    i32x8 pkB = {};
+    int pscB = 127;
     auto iter = [&](auto RR, int j) {
         constexpr int R = decltype(RR)::value;
         constexpr int KRD = KST + ((R + 1) % NST) * TILE, VRD = ((R + 3) % NST) * TILE;
+        f32x16(&sc)[2] = (R & 1) ? sB : s;                 // scores of block j
+        f32x16(&sn)[2] = (R & 1) ? s : sB;                 // scores of block j+1
+        i32x8 &pv_in = (R & 1) ? pkB : pk;                 // P(j-1) and its scale
+        int &psc_in = (R & 1) ? pscB : psc;
+        i32x8 &pv_out = (R & 1) ? pk : pkB;                // P(j)
+        int &psc_out = (R & 1) ? psc : pscB;
+
         sync_vm<2 * VM_ITER>();                            // K(j+1), V(j-1) have landed; stages R, R+2 are free
         dma(krs, KST + R * TILE, so_k, dk);                // K(j+4)
         dma(vrs, VST + ((R + 2) % NST) * TILE, so_v, dv);  // V(j+2)
-        so_k = src_off(list_at(min(j + 5, n - 1)));
-        so_v = src_off(list_at(min(j + 3, n - 1)));
         rescale_o();
         if (diag_last && j == n - 1) {                     // causal mask inside the diagonal block
             asm volatile("");                              // (a real branch: taken once per row)
@@ -991,23 +1007,26 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    if (keymap<kFP8>(2 * ks + t, 8 * (e >> 2) + 4 * g32 + (e & 3)) > qrow) s[t][e] = ninf;
+                    if (keymap<kFP8>(2 * ks + t, 8 * (e >> 2) + 4 * g32 + (e & 3)) > qrow) sc[t][e] = ninf;
         }
-        // ---- one scheduling region: S(j+1) = K(j+1) Q^T under the row max of
-        // S(j), O += V(j-1)^T P(j-1) under the exponentials of block j
-        const i32x8 k00 = kop(KRD, 0, 0), k01 = kop(KRD, 0, 1), k10 = kop(KRD, 1, 0), k11 = kop(KRD, 1, 1);
-        f32x16 sn0 = mfma8(k00, qop(0), f32x16{}, 127);
-        f32x16 sn1 = mfma8(k10, qop(0), f32x16{}, 127);
-        sn0 = mfma8(k01, qop(1), sn0, 127);
-        sn1 = mfma8(k11, qop(1), sn1, 127);
-        float mt[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                mt[4 * t + e] = fmaxf(fmaxf(s[t][4 * e], s[t][4 * e + 1]), fmaxf(s[t][4 * e + 2], s[t][4 * e + 3]));
-        const float mx = max_xor32(fmaxf(fmaxf(fmaxf(mt[0], mt[1]), fmaxf(mt[2], mt[3])),
-                                         fmaxf(fmaxf(mt[4], mt[5]), fmaxf(mt[6], mt[7]))));
+        // ---- the region, in a fixed order: every MFMA is followed by a slice of
+        // the softmax of block j, and every LDS operand is read one MFMA ahead.
+#define SB() __builtin_amdgcn_sched_barrier(0)
+        i32x8 ka = kop(KRD, 0, 0), kb = kop(KRD, 1, 0);
+        i32x8 va = vop(VRD, 0);
+        float m0 = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[0][4], sc[0][5]), fmaxf(sc[0][6], sc[0][7])));
+        float m1 = fmaxf(fmaxf(fmaxf(sc[0][8], sc[0][9]), fmaxf(sc[0][10], sc[0][11])),
+                         fmaxf(fmaxf(sc[0][12], sc[0][13]), fmaxf(sc[0][14], sc[0][15])));
+        SB();
+        sn[0] = mfma8(ka, qop(0), f32x16{}, 127);
+        SB();
+        ka = kop(KRD, 0, 1);
+        float m2 = fmaxf(fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])),
+                         fmaxf(fmaxf(sc[1][4], sc[1][5]), fmaxf(sc[1][6], sc[1][7])));
+        float m3 = fmaxf(fmaxf(fmaxf(sc[1][8], sc[1][9]), fmaxf(sc[1][10], sc[1][11])),
+                         fmaxf(fmaxf(sc[1][12], sc[1][13]), fmaxf(sc[1][14], sc[1][15])));
+        const float mx = max_xor32(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
         const float xm = mx * c;                           // the block's row max in log2 units
         const float Mn = xm > Mthr ? xm : M;               // lazy: move only past M + THRESH
         alpha = __builtin_amdgcn_exp2f(M - Mn);            // 1 unless the max moved
@@ -1017,59 +1036,80 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         // (128, 256]; the PV MFMA multiplies by 2^-e through the E8M0 scale 127 - e.
         const float ce = ceilf(fmaxf(xm - M, -92.0f));     // xm - M <= THRESH, so e >= 0
         const float mc = (M - 8.0f) + ce;
-        const i32x8 v0 = vop(VRD, 0), v1 = vop(VRD, 1);
-        o[0] = mfma8(v0, pk, o[0], psc);
-        const i32x8 v2 = vop(VRD, 2);
-        o[1] = mfma8(v1, pk, o[1], psc);
-        const i32x8 v3 = vop(VRD, 3);
-        o[2] = mfma8(v2, pk, o[2], psc);
-        o[3] = mfma8(v3, pk, o[3], psc);
-        lacc = mfma8(ones, pk, lacc, psc);
+        SB();
+        sn[1] = mfma8(kb, qop(0), f32x16{}, 127);
+        SB();
+        kb = kop(KRD, 1, 1);
         float ls[4];
+        auto expq = [&](int t, int e0) {                  // P of 4 scores, into the partial sums
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(s[t][e], c, -mc));
-                s[t][e] = pe;
-                ls[e & 3] = (t == 0 && e < 4) ? pe : ls[e & 3] + pe;
+            for (int e = e0; e < e0 + 4; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(sc[t][e], c, -mc));
+                sc[t][e] = pe;
+                ls[e & 3] = (t == 0 && e0 == 0) ? pe : ls[e & 3] + pe;
             }
+        };
+        auto packq = [&](int w) {                          // 4 P of P word w as E4M3
+            const f32x16 &src = sc[w >> 2];
+            const int ee = 4 * (w & 3);
+            // the word's old contents (P of block j-2, consumed) are the tied operand
+            const int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], pv_out[w], false);
+            pv_out[w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
+        };
+        expq(0, 0);
+        SB();
+        sn[0] = mfma8(ka, qop(1), sn[0], 127);
+        SB();
+        i32x8 vb = vop(VRD, 1);
+        expq(0, 4);
+        packq(0);
+        SB();
+        sn[1] = mfma8(kb, qop(1), sn[1], 127);
+        SB();
+        expq(0, 8);
+        packq(1);
+        SB();
+        o[0] = mfma8(va, pv_in, o[0], psc_in);
+        SB();
+        va = vop(VRD, 2);
+        expq(0, 12);
+        packq(2);
+        packq(3);
+        SB();
+        o[1] = mfma8(vb, pv_in, o[1], psc_in);
+        SB();
+        vb = vop(VRD, 3);
+        expq(1, 0);
+        SB();
+        o[2] = mfma8(va, pv_in, o[2], psc_in);
+        SB();
+        expq(1, 4);
+        packq(4);
+        SB();
+        o[3] = mfma8(vb, pv_in, o[3], psc_in);
+        SB();
+        expq(1, 8);
+        packq(5);
+        SB();
+        lacc = mfma8(ones, pv_in, lacc, psc_in);
+        SB();
+        expq(1, 12);
+        packq(6);
+        packq(7);
         const int ice = (int)ce;
         l = fmaf(l, alpha, ldexpf((ls[0] + ls[1]) + (ls[2] + ls[3]), ice - 8));
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            const f32x16 &src = s[w >> 2];
-            const int ee = 4 * (w & 3);
-            const int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], __float_as_int(src[ee]), false);
-            pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
-        }
-        psc = 119 + ice;
-        s[0] = sn0;
-        s[1] = sn1;
-        // issue order: K reads, QK MFMAs spaced out by the max tree, V reads, PV
-        // MFMAs spaced out by the exponentials
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        psc_out = 119 + ice;
+        SB();
+#undef SB
+        // ---- lookups, after the region: they complete across the barrier
+        so_k = row_off(tk, pgk);                           // iteration j+1
+        so_v = row_off(tv, pgv);
+        tk = tok_of(__builtin_amdgcn_readfirstlane(lk));   // iteration j+2
+        tv = tok_of(__builtin_amdgcn_readfirstlane(lv));
+        pgk = page_of(tk);
+        pgv = page_of(tv);
+        lk = list_raw(min(j + 7, last));                   // iteration j+3
+        lv = list_raw(min(j + 5, last));
     };
     for (int j = 0; j < n; j += NST) {
         iter(std::integral_constant<int, 0>{}, j);
@@ -1080,10 +1120,14 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     sync_vm<2 * VM_ITER>();                                // V(n-1) has landed
     rescale_o();
     {
+        // block n-1 ran as an iteration with R = (n-1) mod 4: its P is in pkB for even R
+        const bool odd = ((n - 1) & 1) != 0;
+        const i32x8 pl = odd ? pk : pkB;
+        const int sl = odd ? psc : pscB;
         const int vo = ((n - 1) % NST) * TILE;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] = mfma8(vop(vo, dt), pk, o[dt], psc);
-        lacc = mfma8(ones, pk, lacc, psc);
+        for (int dt = 0; dt < 4; ++dt) o[dt] = mfma8(vop(vo, dt), pl, o[dt], sl);
+        lacc = mfma8(ones, pl, lacc, sl);
     }
 
     // ---- merge the key halves, normalise, store -------------------------------
