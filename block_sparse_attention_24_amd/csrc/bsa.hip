@@ -779,13 +779,13 @@ constexpr float M_NONE = -3.0e38f;               // running max before any finit
 __device__ __forceinline__ int swz_k(int key) { return ((key >> 1) & 3) | (((key >> 5) & 1) << 2); }
 __device__ __forceinline__ int swz_v(int key) { return ((key >> 1) & 3) << 1; }
 
-// s_waitcnt vmcnt(VM) lgkmcnt(0), then the workgroup barrier.  The barrier
-// itself waits for nothing, so the last VM loads into LDS stay in flight
-// across it.
-template <int VM>
+// s_waitcnt vmcnt(VM) (and lgkmcnt(0) if LGKM), then the workgroup barrier.
+// The barrier itself waits for nothing, so the last VM loads into LDS stay in
+// flight across it.
+template <int VM, bool LGKM = false>
 __device__ __forceinline__ void sync_vm() {
     static_assert(VM < 64, "vmcnt is six bits");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((LGKM ? 0 : 15) << 8) | ((VM >> 4) << 14));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -800,12 +800,14 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void *p) {
 }
 
 // 16 bytes per lane from global memory (descriptor + soff + voff) straight
-// into LDS at byte m0 + 16 * lane.  Written as asm so that the compiler, which
-// would otherwise make every later transposing LDS read wait for all such loads,
-// leaves the pacing to the explicit vmcnt waits; the asm has no outputs.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned m0, unsigned voff, unsigned soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+// into LDS at byte lds + OFF + 16 * lane.  Written as asm so that the compiler,
+// which would otherwise make every later transposing LDS read wait for all such
+// loads, leaves the pacing to the explicit vmcnt waits.  The asm has no
+// outputs; m0 is used by nothing else in these kernels.
+template <int OFF>
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned lds, unsigned voff, unsigned soff) {
+    asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF) : "memory", "m0");
 }
 }  // namespace fp8p
 
@@ -892,10 +894,12 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     auto list_raw = [&](int i) -> int { return SPARSE ? (int)list[i] : i; };
     const i32x4 krs = buffer_rsrc(a.k), vrs = buffer_rsrc(a.v);
     const unsigned lds_wave = (unsigned)(size_t)(lds_char *)smem + 16 * wave * D;   // this wave's rows in a stage
-    auto dma = [&](i32x4 rs, int stage_off, unsigned so, const int (&vo)[2]) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) load_lds16(rs, lds_wave + stage_off + 8 * i * D, (unsigned)vo[i], so);
+    auto dma = [&](i32x4 rs, auto STAGE_OFF, unsigned so, const int (&vo)[2]) {
+        constexpr int OFF = decltype(STAGE_OFF)::value;
+        load_lds16<OFF>(rs, lds_wave, (unsigned)vo[0], so);
+        load_lds16<OFF + 8 * D>(rs, lds_wave, (unsigned)vo[1], so);
     };
+    using std::integral_constant;
 
     auto qop = [&](int st) {
         const u32x4 b0 = qf.u[2 * st], b1 = qf.u[2 * st + 1];
@@ -943,13 +947,13 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     {
         const unsigned s0 = src_off(list_at(0));
         const unsigned s1 = src_off(list_at(min(1, last)));
-        dma(krs, KST, s0, dk);
-        dma(krs, KST + TILE, s1, dk);
-        dma(vrs, VST + 3 * TILE, s0, dv);
-        dma(krs, KST + 2 * TILE, src_off(list_at(min(2, last))), dk);
-        dma(vrs, VST, s0, dv);
-        dma(krs, KST + 3 * TILE, src_off(list_at(min(3, last))), dk);
-        dma(vrs, VST + TILE, s1, dv);
+        dma(krs, integral_constant<int, KST>{}, s0, dk);
+        dma(krs, integral_constant<int, KST + TILE>{}, s1, dk);
+        dma(vrs, integral_constant<int, VST + 3 * TILE>{}, s0, dv);
+        dma(krs, integral_constant<int, KST + 2 * TILE>{}, src_off(list_at(min(2, last))), dk);
+        dma(vrs, integral_constant<int, VST>{}, s0, dv);
+        dma(krs, integral_constant<int, KST + 3 * TILE>{}, src_off(list_at(min(3, last))), dk);
+        dma(vrs, integral_constant<int, VST + TILE>{}, s1, dv);
     }
     // Row lookups run ahead of the loads that use them, so that no wave waits
     // on them: the list entry is read at the end of iteration i-3, the page
@@ -959,7 +963,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     int tk = tok_of(list_at(min(5, last))), tv = tok_of(list_at(min(3, last)));             // iteration 1
     int pgk = page_of(tk), pgv = page_of(tv);
     int lk = list_raw(min(6, last)), lv = list_raw(min(4, last));                          // iteration 2
-    sync_vm<3 * VM_ITER>();                                // K(0) has landed
+    sync_vm<3 * VM_ITER, true>();                          // K(0) has landed
 #pragma unroll
     for (int t = 0; t < 2; ++t) s[t] = mfma8(kop(KST, t, 1), qop(1), mfma8(kop(KST, t, 0), qop(0), f32x16{}, 127), 127);
 
@@ -997,9 +1001,10 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         i32x8 &pv_out = (R & 1) ? pk : pkB;                // P(j)
         int &psc_out = (R & 1) ? psc : pscB;
 
-        sync_vm<2 * VM_ITER>();                            // K(j+1), V(j-1) have landed; stages R, R+2 are free
-        dma(krs, KST + R * TILE, so_k, dk);                // K(j+4)
-        dma(vrs, VST + ((R + 2) % NST) * TILE, so_v, dv);  // V(j+2)
+        // K(j+1), V(j-1) have landed; stages R, R+2 are free.  (The lookups issued
+        // at the end of the last iteration are waited for here, inside the
+        // barrier's own skew, rather than at the first LDS wait of the region.)
+        sync_vm<2 * VM_ITER, true>();
         rescale_o();
         if (diag_last && j == n - 1) {                     // causal mask inside the diagonal block
             asm volatile("");                              // (a real branch: taken once per row)
@@ -1011,6 +1016,11 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         }
         // ---- the region, in a fixed order: every MFMA is followed by a slice of
         // the softmax of block j, and every LDS operand is read one MFMA ahead.
+        // The loads of K(j+4) and V(j+2) into LDS are spread over it, so that
+        // the waves of the workgroup do not all queue them behind the barrier.
+        constexpr int KDM = KST + R * TILE, VDM = VST + ((R + 2) % NST) * TILE;   // stages being loaded
+        auto dma_k = [&](auto I) { load_lds16<KDM + 8 * decltype(I)::value * D>(krs, lds_wave, (unsigned)dk[I], so_k); };
+        auto dma_v = [&](auto I) { load_lds16<VDM + 8 * decltype(I)::value * D>(vrs, lds_wave, (unsigned)dv[I], so_v); };
 #define SB() __builtin_amdgcn_sched_barrier(0)
         i32x8 ka = kop(KRD, 0, 0), kb = kop(KRD, 1, 0);
         i32x8 va = vop(VRD, 0);
@@ -1021,6 +1031,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         SB();
         sn[0] = mfma8(ka, qop(0), f32x16{}, 127);
         SB();
+        dma_k(integral_constant<int, 0>{});
         ka = kop(KRD, 0, 1);
         float m2 = fmaxf(fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])),
                          fmaxf(fmaxf(sc[1][4], sc[1][5]), fmaxf(sc[1][6], sc[1][7])));
@@ -1039,6 +1050,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         SB();
         sn[1] = mfma8(kb, qop(0), f32x16{}, 127);
         SB();
+        dma_k(integral_constant<int, 1>{});
         kb = kop(KRD, 1, 1);
         float ls[4];
         auto expq = [&](int t, int e0) {                  // P of 4 scores, into the partial sums
@@ -1060,12 +1072,14 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         SB();
         sn[0] = mfma8(ka, qop(1), sn[0], 127);
         SB();
+        dma_v(integral_constant<int, 0>{});
         i32x8 vb = vop(VRD, 1);
         expq(0, 4);
         packq(0);
         SB();
         sn[1] = mfma8(kb, qop(1), sn[1], 127);
         SB();
+        dma_v(integral_constant<int, 1>{});
         expq(0, 8);
         packq(1);
         SB();
@@ -1133,7 +1147,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     // ---- merge the key halves, normalise, store -------------------------------
     l = sum_xor32(l);                                      // exact sum of P: the LSE
     float lq = lacc[0];                                    // sum of the quantised P: O's denominator
-    sync_vm<0>();                                          // every load into LDS is done: stages are free
+    sync_vm<0, true>();                                    // every load into LDS is done: stages are free
     float *po = reinterpret_cast<float *>(smem) + wq * 64 * (D / 2);
     if (ks == 1) {
 #pragma unroll
