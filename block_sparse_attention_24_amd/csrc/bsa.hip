@@ -807,7 +807,8 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void *p) {
 template <int OFF>
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned lds, unsigned voff, unsigned soff) {
     asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF) : "memory", "m0");
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                    "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(OFF) : "memory", "m0");
 }
 }  // namespace fp8p
 
@@ -926,7 +927,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, 0, 0, 0, 127, 0, sy);
     };
     const int one = 0x38383838;                            // four E4M3 1.0
-    const i32x8 ones = {one, one, one, one, one, one, one, one};
+    i32x8 ones = {one, one, one, one, one, one, one, one};
 
     const float c = a.c_exp2;
     const float ninf = -__builtin_huge_valf();
@@ -1005,6 +1006,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         // at the end of the last iteration are waited for here, inside the
         // barrier's own skew, rather than at the first LDS wait of the region.)
         sync_vm<2 * VM_ITER, true>();
+        asm volatile("" : "+v"(ones));                     // kept in registers, not rebuilt per block
         rescale_o();
         if (diag_last && j == n - 1) {                     // causal mask inside the diagonal block
             asm volatile("");                              // (a real branch: taken once per row)
@@ -1024,20 +1026,21 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
 #define SB() __builtin_amdgcn_sched_barrier(0)
         i32x8 ka = kop(KRD, 0, 0), kb = kop(KRD, 1, 0);
         i32x8 va = vop(VRD, 0);
-        float m0 = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[0][4], sc[0][5]), fmaxf(sc[0][6], sc[0][7])));
-        float m1 = fmaxf(fmaxf(fmaxf(sc[0][8], sc[0][9]), fmaxf(sc[0][10], sc[0][11])),
-                         fmaxf(fmaxf(sc[0][12], sc[0][13]), fmaxf(sc[0][14], sc[0][15])));
+        // row max: a tree of three-input maxima (v_max3), 16 for the 32 scores
+        auto max3 = [](float x, float y, float z) { return fmaxf(x, fmaxf(y, z)); };
+        auto tile_max = [&](const f32x16 &x, float &u, float &v) {
+            u = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8]));
+            v = max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]);
+        };
+        float m0, m1, m2, m3;
+        tile_max(sc[0], m0, m1);
         SB();
         sn[0] = mfma8(ka, qop(0), f32x16{}, 127);
         SB();
         dma_k(integral_constant<int, 0>{});
         ka = kop(KRD, 0, 1);
-        float m2 = fmaxf(fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])),
-                         fmaxf(fmaxf(sc[1][4], sc[1][5]), fmaxf(sc[1][6], sc[1][7])));
-        float m3 = fmaxf(fmaxf(fmaxf(sc[1][8], sc[1][9]), fmaxf(sc[1][10], sc[1][11])),
-                         fmaxf(fmaxf(sc[1][12], sc[1][13]), fmaxf(sc[1][14], sc[1][15])));
-        const float mx = max_xor32(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+        tile_max(sc[1], m2, m3);
+        const float mx = max_xor32(fmaxf(max3(m0, m1, m2), m3));
         const float xm = mx * c;                           // the block's row max in log2 units
         const float Mn = xm > Mthr ? xm : M;               // lazy: move only past M + THRESH
         alpha = __builtin_amdgcn_exp2f(M - Mn);            // 1 unless the max moved
