@@ -24,7 +24,7 @@ import block_sparse_attention_24_amd as sb
 import oracle
 import workloads as wl
 from gpu_common import (TOL_LSE, TOL_O, TOL_SCORE, mask_bits, near_tie_diff, oracle_qkv,
-                        output_error, problem, run_path, workspace_views, kv_args)
+                        output_error, problem, run_path, tol_o, workspace_views, kv_args)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,8 +109,38 @@ def test_small_full_oracle(w):
     o, lse = sb.attention(p, inp["q"], k_, v_, words, table, page)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.block_sparse_attention(q, k, v, m_ref, w.block)
-    assert output_error(o, o_ref) < TOL_O[w.dtype]
+    assert output_error(o, o_ref) < tol_o(w)
     assert np.max(np.abs(lse.cpu().double().numpy() - lse_ref)) < TOL_LSE[w.dtype]
+
+
+# fp8 at unit-variance inputs (no sink scaling, V rows unscaled): the bar of
+# max-abs 6e-2 applies as stated.  Both fp8 kernels (d = 128 with 128-token
+# blocks, and the other shapes), paged and contiguous, several seeds.
+FP8_UNIT = [
+    wl.Workload(f"fp8-unit-s{s}-b{blk}-d{d}{'-paged' if paged else ''}", 1, blk * n, hq, hkv, d, blk, "fp8",
+                density=dens, sink=False, v_sigma=0.0, paged=paged, page_size=64, seed=s)
+    for s, (blk, d, n, hq, hkv, dens, paged) in enumerate([
+        (128, 128, 40, 8, 1, 0.25, True), (128, 128, 33, 8, 2, 0.4, False), (128, 128, 48, 4, 2, 0.25, True),
+        (128, 128, 24, 8, 2, 0.7, False), (128, 128, 56, 8, 1, 0.3, True), (64, 64, 50, 4, 2, 0.25, False),
+        (128, 64, 33, 2, 2, 0.25, False), (64, 128, 41, 4, 1, 0.4, False)], start=11)]
+
+
+@pytest.mark.parametrize("w", FP8_UNIT, ids=lambda w: w.name)
+def test_fp8_unit_variance_bar(w):
+    _announce(f"fp8 unit-variance {w.name}")
+    assert tol_o(w) == TOL_O["fp8"]
+    inp = wl.make_inputs(w, device=DEV)
+    q, k, v = oracle_qkv(inp)
+    nb = w.num_blocks
+    budget, _ = oracle.tpd_budget(nb, w.density, w.alpha)
+    m_ref = oracle.select_blocks(oracle.oam_scores(q, k, v, w.block), budget)
+    words = torch.from_numpy(oracle.pack_block_mask(m_ref).view(np.int32)).to(DEV)
+    k_, v_, table, page = kv_args(w, inp)
+    o, lse = sb.attention(problem(w, inp), inp["q"], k_, v_, words, table, page)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.block_sparse_attention(q, k, v, m_ref, w.block)
+    assert output_error(o, o_ref) < TOL_O["fp8"]
+    assert np.max(np.abs(lse.cpu().double().numpy() - lse_ref)) < TOL_LSE["fp8"]
 
 
 @pytest.mark.parametrize("w", [SMALL[0], SMALL[2], SMALL[6]], ids=lambda w: w.name)
@@ -131,7 +161,7 @@ def test_dense_kernel_equals_oracle_and_full_mask(w):
     q, k, v = oracle_qkv(inp)
     o_ref, l_ref = oracle.dense_causal_attention(q, k, v) if w.seq <= 2048 else \
         oracle.block_sparse_attention(q, k, v, np.ones((w.batch, w.hq, nb, nb), dtype=bool), w.block)
-    assert output_error(o_d, o_ref) < TOL_O[w.dtype]
+    assert output_error(o_d, o_ref) < tol_o(w)
     assert np.max(np.abs(l_d.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
 
 
@@ -227,7 +257,7 @@ def test_zero_value_block():
 # Full-size workloads, in the launch configuration the bench times.
 # --------------------------------------------------------------------------
 
-def _sampled_check(w, inp, out, rows_per_head=12, heads=4, seed=0):
+def _sampled_check(w, inp, out, rows_per_head=12, heads=4, seed=0, gen_device=DEV):
     """Scores of whole sampled heads (oracle, fp64), exact selection on the
     GPU's scores of those heads, attention on sampled rows with the GPU mask."""
     nb = w.num_blocks
@@ -259,7 +289,7 @@ def _sampled_check(w, inp, out, rows_per_head=12, heads=4, seed=0):
         o_ref, l_ref = oracle.attention_rows(qh, kh, vh, m_gpu, w.block, sub)
         o_g = out["o"][0, [t for (_, _, t) in sub], h]
         l_g = out["lse"][0, h, [t for (_, _, t) in sub]]
-        assert output_error(o_g, o_ref) < TOL_O[w.dtype], h
+        assert output_error(o_g, o_ref) < tol_o(w, gen_device), h
         assert np.max(np.abs(l_g.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype], h
 
 
@@ -285,7 +315,7 @@ def test_full_8k_whole_oracle(w):
     o, lse = sb.attention(out["p"], inp["q"], inp["k"], inp["v"], words)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.block_sparse_attention(q, k, v, m_ref, w.block)
-    assert output_error(o, o_ref) < TOL_O[w.dtype]
+    assert output_error(o, o_ref) < tol_o(w)
     assert np.max(np.abs(lse.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
 
 
@@ -307,7 +337,7 @@ def test_full_size_sampled(w):
     vh = oracle.dequantize(wl.to_float64(inp["v"][:, :, g:g + 1]), inp["v_scale"])
     toks = [0, 1, 127, 128, w.seq // 2 + 5, w.seq - 1]
     o_ref, l_ref = oracle.attention_rows(qh, kh, vh, None, w.block, [(0, 0, t) for t in toks])
-    assert output_error(o_d[0, toks, h], o_ref) < TOL_O[w.dtype]
+    assert output_error(o_d[0, toks, h], o_ref) < tol_o(w, DEV)
     assert np.max(np.abs(l_d[0, h, toks].cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
 
 

@@ -40,6 +40,7 @@ class Workload:
     paged: bool = False
     page_size: int = 64
     seed: int = 0
+    v_sigma: float = 0.5        # V row scale ~ LogNormal(0, v_sigma); 0 gives unit-variance V
 
     @property
     def num_blocks(self) -> int:
@@ -50,7 +51,7 @@ class Workload:
                 "q_heads": self.hq, "kv_heads": self.hkv, "head_dim": self.head_dim,
                 "block": self.block, "dtype": self.dtype, "density": self.density,
                 "alpha": self.alpha, "paged_kv": self.paged,
-                "page_size": self.page_size if self.paged else None}
+                "page_size": self.page_size if self.paged else None, "v_sigma": self.v_sigma}
 
 
 # The five workloads of the measurement plan, smallest first.
@@ -82,6 +83,12 @@ def quantize_fp8(x: torch.Tensor):
     return codes, scale
 
 
+def v_row_scale(w: Workload, gen_device: Optional[str] = None) -> torch.Tensor:
+    """The per-token V row scales ([b, S], on gen_device) that make_inputs
+    applies: exp(v_sigma * N(0, 1)) from seed + 3."""
+    return torch.exp(w.v_sigma * _randn((w.batch, w.seq), w.seed + 3, gen_device or "cpu"))
+
+
 def make_inputs(w: Workload, device="cpu", gen_device: Optional[str] = None):
     """Returns a dict with
       q [b, S, Hq, d], k/v [b, S, Hkv, d]      working dtype (fp8: E4M3 codes)
@@ -96,8 +103,7 @@ def make_inputs(w: Workload, device="cpu", gen_device: Optional[str] = None):
     q = _randn((b, S, hq, d), w.seed, gd)
     k = _randn((b, S, hkv, d), w.seed + 1, gd)
     v = _randn((b, S, hkv, d), w.seed + 2, gd)
-    s = torch.exp(0.5 * _randn((b, S), w.seed + 3, gd))
-    v.mul_(s[:, :, None, None])
+    v.mul_(v_row_scale(w, gd)[:, :, None, None])
     if w.sink:
         k[:, :4].mul_(4.0)
     out = {"q_scale": 1.0, "k_scale": 1.0, "v_scale": 1.0}
