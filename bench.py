@@ -14,6 +14,7 @@ paged K/V (64-token pages, random page order), TPD density 1/4.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -151,9 +152,7 @@ def main():
 
     w = WORKLOADS[args.workload]
     if args.density is not None:
-        w = wl.Workload(w.name, w.batch, w.seq, w.hq, w.hkv, w.head_dim, w.block, w.dtype,
-                        density=args.density, alpha=w.alpha, sink=w.sink, paged=w.paged,
-                        page_size=w.page_size, seed=w.seed)
+        w = dataclasses.replace(w, density=args.density)
     dev = "cuda"
     torch.cuda.init()
     log(f"[bench] workload {w.name} density {w.density}: generating inputs", )

@@ -14,6 +14,7 @@ sampled rows.  Every case prints its name before it touches the GPU."""
 
 from __future__ import annotations
 
+import dataclasses
 import math
 
 import numpy as np
@@ -346,8 +347,7 @@ def test_density_sweep_64k_sampled():
     base = wl.GQA_64K
     inp = wl.make_inputs(base, device=DEV, gen_device=DEV)
     for dens in (0.8, 0.5, 0.2):
-        w = wl.Workload(base.name + f"-d{dens}", base.batch, base.seq, base.hq, base.hkv,
-                        base.head_dim, base.block, base.dtype, density=dens)
+        w = dataclasses.replace(base, name=base.name + f"-d{dens}", density=dens)
         _announce(w.name)
         out = run_path(w, inp, density=dens)
         _sampled_check(w, inp, out, rows_per_head=6, heads=2, seed=int(dens * 10))
