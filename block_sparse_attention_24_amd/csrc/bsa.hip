@@ -878,12 +878,18 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         dv[i] = (8 * i + (lane >> 3)) * (int)row_bytes + ((cl ^ swz_v(row)) << 4);
     }
     auto list_at = [&](int i) { return SPARSE ? __builtin_amdgcn_readfirstlane((int)list[i]) : i; };
+    const int last = n - 1;
+    if constexpr (SPARSE) {
+        // pad the list with copies of its last entry, so that reads up to 8 entries
+        // ahead need no clamp (visible after the prologue's barrier)
+        if (tid < 8) list[n + tid] = list[last];
+    }
     // The block table is read-only here: reading it through the constant
     // address space makes the lookups scalar loads, off the vector memory
     // counter that paces the loads into LDS.
-    const_i32 *table = (const_i32 *)a.table;
+    const_i32 *table = PAGED ? (const_i32 *)a.table + b * a.pages_per_seq : nullptr;   // this row's pages
     // byte offset of this wave's first row of a block: its token, and its page when paged
-    auto page_of = [&](int tok) -> int { return PAGED ? table[b * a.pages_per_seq + (tok >> a.page_log2)] : 0; };
+    auto page_of = [&](int tok) -> int { return PAGED ? table[(unsigned)tok >> a.page_log2] : 0; };
     auto row_off = [&](int tok, int page) -> unsigned {
         unsigned row;
         if constexpr (PAGED) row = ((unsigned)page << a.page_log2) | (unsigned)(tok & ((1 << a.page_log2) - 1));
@@ -892,7 +898,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     };
     auto tok_of = [&](int J) { return J * BLK + 16 * wave; };
     auto src_off = [&](int J) -> unsigned { return row_off(tok_of(J), page_of(tok_of(J))); };
-    auto list_raw = [&](int i) -> int { return SPARSE ? (int)list[i] : i; };
+    auto list_raw = [&](int i) -> int { return SPARSE ? (int)list[i] : min(i, last); };   // i <= n + 7
     const i32x4 krs = buffer_rsrc(a.k), vrs = buffer_rsrc(a.v);
     const unsigned lds_wave = (unsigned)(size_t)(lds_char *)smem + 16 * wave * D;   // this wave's rows in a stage
     auto dma = [&](i32x4 rs, auto STAGE_OFF, unsigned so, const int (&vo)[2]) {
@@ -938,13 +944,12 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     f32x16 s[2];                                           // scores of the block awaiting softmax
     i32x8 pk = {};                                         // P of the block awaiting PV, E4M3
     int psc = 127;                                         // its E8M0 scale
-    const bool diag_last = list_at(n - 1) == I;            // the diagonal block, if kept, is the last
+    const int jdiag = list_at(last) == I ? last : -1;     // the diagonal block, if kept, is the last
 
     // ---- prologue --------------------------------------------------------------
     // As if iterations -3 .. -1 had run: K(0..3) and V(0..1) loading, V(-1)
     // standing in V stage 3 (a copy of V(0): the first PV multiplies it by
     // P = 0, so it only has to be finite, which V(0) is wherever O is).
-    const int last = n - 1;
     {
         const unsigned s0 = src_off(list_at(0));
         const unsigned s1 = src_off(list_at(min(1, last)));
@@ -1008,7 +1013,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         sync_vm<2 * VM_ITER, true>();
         asm volatile("" : "+v"(ones));                     // kept in registers, not rebuilt per block
         rescale_o();
-        if (diag_last && j == n - 1) {                     // causal mask inside the diagonal block
+        if (j == jdiag) {                                  // causal mask inside the diagonal block
             asm volatile("");                              // (a real branch: taken once per row)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -1125,8 +1130,8 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         tv = tok_of(__builtin_amdgcn_readfirstlane(lv));
         pgk = page_of(tk);
         pgv = page_of(tv);
-        lk = list_raw(min(j + 7, last));                   // iteration j+3
-        lv = list_raw(min(j + 5, last));
+        lk = list_raw(j + 7);                              // iteration j+3
+        lv = list_raw(j + 5);
     };
     for (int j = 0; j < n; j += NST) {
         iter(std::integral_constant<int, 0>{}, j);
