@@ -969,15 +969,17 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     int tk = tok_of(list_at(min(5, last))), tv = tok_of(list_at(min(3, last)));             // iteration 1
     int pgk = page_of(tk), pgv = page_of(tv);
     int lk = list_raw(min(6, last)), lv = list_raw(min(4, last));                          // iteration 2
-    sync_vm<3 * VM_ITER, true>();                          // K(0) has landed
+    sync_vm<10, true>();                                   // K(0) and K(1) have landed
 #pragma unroll
     for (int t = 0; t < 2; ++t) s[t] = mfma8(kop(KST, t, 1), qop(1), mfma8(kop(KST, t, 0), qop(0), f32x16{}, 127), 127);
+    i32x8 kfirst = kop(KST + TILE, 0, 0);                  // first K operand of S(1)
 
     // ---- main loop: iteration j = softmax(j) with QK(j+1) and PV(j-1) ---------
     // Stages (R = j mod 4): K(j+1) is read from K stage R+1 while K(j+4) loads
     // into K stage R; V(j-1) is read from V stage R+3 while V(j+2) loads into V
     // stage R+2.  Every iteration issues VM_ITER loads per wave, so "all but the
-    // last 2 VM_ITER" are the loads of iteration j-3.
+    // last VM_ITER" are the loads of iterations up to j-2: K(j+2) is then in LDS
+    // too, and the first K operand of the next block is read at the end of this one.
     float alpha = 1.0f;                                    // rescale of O and lacc still to apply
     auto rescale_o = [&]() {
         // O holds the PV MFMAs up to block j-2 at the scale of M before block
@@ -1007,10 +1009,10 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         i32x8 &pv_out = (R & 1) ? pk : pkB;                // P(j)
         int &psc_out = (R & 1) ? psc : pscB;
 
-        // K(j+1), V(j-1) have landed; stages R, R+2 are free.  (The lookups issued
-        // at the end of the last iteration are waited for here, inside the
+        // K(j+1), K(j+2), V(j-1) have landed; stages R, R+2 are free.  (The lookups
+        // issued at the end of the last iteration are waited for here, inside the
         // barrier's own skew, rather than at the first LDS wait of the region.)
-        sync_vm<2 * VM_ITER, true>();
+        sync_vm<VM_ITER, true>();
         asm volatile("" : "+v"(ones));                     // kept in registers, not rebuilt per block
         rescale_o();
         if (j == jdiag) {                                  // causal mask inside the diagonal block
@@ -1029,7 +1031,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         auto dma_k = [&](auto I) { load_lds16<KDM + 8 * decltype(I)::value * D>(krs, lds_wave, (unsigned)dk[I], so_k); };
         auto dma_v = [&](auto I) { load_lds16<VDM + 8 * decltype(I)::value * D>(vrs, lds_wave, (unsigned)dv[I], so_v); };
 #define SB() __builtin_amdgcn_sched_barrier(0)
-        i32x8 ka = kop(KRD, 0, 0), kb = kop(KRD, 1, 0);
+        i32x8 ka = kfirst, kb = kop(KRD, 1, 0);
         i32x8 va = vop(VRD, 0);
         // row max: a tree of three-input maxima (v_max3), 16 for the 32 scores
         auto max3 = [](float x, float y, float z) { return fmaxf(x, fmaxf(y, z)); };
@@ -1087,6 +1089,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         SB();
         sn[1] = mfma8(kb, qop(1), sn[1], 127);
         SB();
+        kfirst = kop(KST + ((R + 2) % NST) * TILE, 0, 0);  // K(j+2): the first operand of S(j+2)
         dma_v(integral_constant<int, 1>{});
         expq(0, 8);
         packq(1);
