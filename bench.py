@@ -15,9 +15,11 @@ from __future__ import annotations
 
 import argparse
 import dataclasses
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -34,6 +36,29 @@ PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "f32": 157.3}   # MI355X dense MFM
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {w.name: w for w in wl.ALL}
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_24_amd", "csrc", "bsa.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def attn_kernel_name(w: wl.Workload) -> str:
+    return "bsa_fp8_kernel" if (w.dtype, w.head_dim, w.block) == ("fp8", 128, 128) else "bsa_kernel"
+
+
+def measured_traffic(w: wl.Workload, kernel: str):
+    """HBM bytes per launch of the sparse attention kernel on workload w, from
+    the rocprofv3 FETCH_SIZE/WRITE_SIZE summaries under profiles/ (a line
+    `traffic: <kernel> <workload> density=<d> bytes=<n> source_sha256=<h>`).
+    None if no summary covers this kernel and workload, or if the attention
+    source has changed since the counters were taken."""
+    with open(ATTN_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    pat = re.compile(r"traffic: (\S+) (\S+) density=(\S+) bytes=(\d+) source_sha256=([0-9a-f]+)")
+    for name in sorted(os.listdir(PROFILES)) if os.path.isdir(PROFILES) else []:
+        with open(os.path.join(PROFILES, name), encoding="utf-8") as f:
+            for m in pat.finditer(f.read()):
+                if (m.group(1), m.group(2), float(m.group(3))) == (kernel, w.name, w.density) and m.group(5) == sha:
+                    return int(m.group(4))
+    return None
 
 
 def log(*a):
@@ -233,9 +258,12 @@ def main():
         "score_hbm_frac": score_bytes(w) / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
     peak = PEAK_TFLOPS[w.dtype]
-    result["roofline"] = {"bound": "mfma", "kernel": "bsa_kernel (sparse)",
+    kname = attn_kernel_name(w)
+    traffic = measured_traffic(w, kname)
+    result["roofline"] = {"bound": "mfma", "kernel": kname + " (sparse)",
                           "achieved": result["bsa_kept_tflops"], "peak": peak, "unit": "TFLOP/s",
-                          "frac": result["bsa_kept_tflops"] / peak, "traffic": None}
+                          "frac": result["bsa_kept_tflops"] / peak, "traffic": traffic,
+                          "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
 
     if not args.no_dense:
         log(f"[bench] dense baseline and density-1 sparse run, {args.dense_steps} each")
