@@ -44,14 +44,22 @@ def attn_kernel_name(w: wl.Workload) -> str:
     return "bsa_fp8_kernel" if (w.dtype, w.head_dim, w.block) == ("fp8", 128, 128) else "bsa_kernel"
 
 
+def attn_source_hash() -> str:
+    """sha256 of the attention source with comments and whitespace removed, so
+    that only a change of the code itself retires a recorded measurement."""
+    with open(ATTN_SRC, encoding="utf-8") as f:
+        code = "".join(line.split("//", 1)[0] for line in f)
+    return hashlib.sha256("".join(code.split()).encode()).hexdigest()
+
+
 def measured_traffic(w: wl.Workload, kernel: str):
     """HBM bytes per launch of the sparse attention kernel on workload w, from
     the rocprofv3 FETCH_SIZE/WRITE_SIZE summaries under profiles/ (a line
-    `traffic: <kernel> <workload> density=<d> bytes=<n> source_sha256=<h>`).
-    None if no summary covers this kernel and workload, or if the attention
-    source has changed since the counters were taken."""
-    with open(ATTN_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    `traffic: <kernel> <workload> density=<d> bytes=<n> source_sha256=<h>`,
+    h = attn_source_hash() when the counters were taken).  None if no summary
+    covers this kernel and workload, or if the attention code has changed since.
+    Run `python bench.py --source-hash` to print the current hash."""
+    sha = attn_source_hash()
     pat = re.compile(r"traffic: (\S+) (\S+) density=(\S+) bytes=(\d+) source_sha256=([0-9a-f]+)")
     for name in sorted(os.listdir(PROFILES)) if os.path.isdir(PROFILES) else []:
         with open(os.path.join(PROFILES, name), encoding="utf-8") as f:
@@ -167,9 +175,14 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="print the attention source hash recorded next to measured traffic, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.source_hash:
+        print(attn_source_hash())
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

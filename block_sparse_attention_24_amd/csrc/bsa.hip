@@ -6,23 +6,28 @@
 // as the baseline (§二.3) is the same template without any mask logic.
 //
 // Design for gfx950 (wave64, 32x32 MFMA, 160 KiB LDS):
-//   * One workgroup per (batch, head, query block I); BLK/32 waves, each wave
-//     owns 32 query rows.  Workgroups run heaviest-first (I descending), and
-//     the heads that share a KV head are spread so that they land on one XCD
-//     (workgroup ids go round-robin over the 8 XCDs), to reuse K/V in its L2.
+//   * One workgroup per (batch, head, query block I) with 2 * BLK/32 waves:
+//     each 32-row query group has two waves, each taking half of every key
+//     block, so every SIMD runs two waves; their partial softmax states are
+//     merged through LDS at the end.  Workgroups run heaviest-first (I
+//     descending), and the heads that share a KV head are spread so that they
+//     land on one XCD (workgroup ids go round-robin over the 8 XCDs), to reuse
+//     K/V in its L2.
 //   * S^T = K Q^T on MFMA (keys are the M dimension), so after the MFMA every
 //     lane holds one query's scores: the row max needs one cross-lane swap
 //     (lane ^ 32) and the running sum none until the end.
 //   * O^T += V^T P^T: the probabilities stay in registers as the B operand.
 //     The K rows are fed to the first MFMA in a permuted order chosen so that
-//     the keys a lane holds afterwards are contiguous in V^T, making every
-//     LDS read a 16-byte vector read.
-//   * K is staged in LDS as [key][d], V transposed as [d][key] (a register
-//     transpose on the way in); 16-byte chunks are XOR-swizzled by row to
-//     keep the vector reads bank-conflict free.  Two LDS stages: the next
-//     block's global loads are in flight while the current one is computed.
-//   * bf16: v_mfma_f32_32x32x16_bf16; fp8 (OCP E4M3): v_mfma_f32_32x32x64_f8f6f4
-//     with P scaled by 256 before its fp8 cast; fp32: v_mfma_f32_32x32x2f32.
+//     the keys a lane holds afterwards are contiguous in V; V is read with the
+//     transposing LDS loads (ds_read_b64_tr_b8 / tr_b16).  K and V sit in LDS
+//     as [key][d] with 16-byte chunks swizzled by row.
+//   * bf16: v_mfma_f32_32x32x16_bf16; fp32: v_mfma_f32_32x32x2f32; fp8 (OCP
+//     E4M3): v_mfma_f32_32x32x64_f8f6f4 with P cast per query and block as
+//     P * 2^e and the E8M0 operand scale undoing 2^e.
+//   * Two kernels.  bsa_fp8_kernel (fp8, d = 128, 128-token blocks) is a
+//     software pipeline that loads K/V straight into LDS; bsa_kernel (all other
+//     shapes) alternates MFMA and softmax phases between the two waves of a
+//     SIMD, with register-staged loads.  Each is described where it is defined.
 #include <type_traits>
 
 #include "device_common.h"
