@@ -192,31 +192,69 @@ def test_run_twice_bit_identical():
         assert torch.equal(x, y)
 
 
-def test_empty_rows_and_bits_above_diagonal():
-    w = wl.Workload("edge-masks", 1, 128 * 9, 2, 1, 128, 128, "bf16")
+EDGE = [wl.Workload("edge-masks-bf16", 1, 128 * 9, 2, 1, 128, 128, "bf16"),
+        wl.Workload("edge-masks-fp8-paged16", 1, 128 * 9, 2, 1, 128, 128, "fp8", paged=True, page_size=16,
+                    sink=False, v_sigma=0.0)]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
+def test_empty_rows_and_bits_above_diagonal(w):
     _announce(w.name)
     inp = wl.make_inputs(w, device=DEV)
     p = problem(w, inp)
+    k_, v_, table, page = kv_args(w, inp)
     nb = w.num_blocks
     rng = np.random.default_rng(5)
     m = np.tril(rng.random((1, 2, nb, nb)) < 0.5)
     m[0, 0, 4, :] = False                     # an empty row
     m[0, 1, 0, :] = False                     # the very first row empty
     words = torch.from_numpy(oracle.pack_block_mask(m).view(np.int32)).to(DEV)
-    o1, l1 = sb.attention(p, inp["q"], inp["k"], inp["v"], words)
+    o1, l1 = sb.attention(p, inp["q"], k_, v_, words, table, page)
     m2 = m | np.triu(np.ones((nb, nb), dtype=bool), 1)        # junk above the diagonal
     words2 = torch.from_numpy(oracle.pack_block_mask(m2).view(np.int32)).to(DEV)
-    o2, l2 = sb.attention(p, inp["q"], inp["k"], inp["v"], words2)
+    o2, l2 = sb.attention(p, inp["q"], k_, v_, words2, table, page)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     q, k, v = oracle_qkv(inp)
     o_ref, l_ref = oracle.block_sparse_attention(q, k, v, m, w.block)
-    assert output_error(o1, o_ref) < TOL_O["bf16"]
+    assert output_error(o1, o_ref) < tol_o(w)
     lg = l1.cpu().double().numpy()
     assert np.all(np.isneginf(lg[0, 0, 4 * 128:5 * 128])) and np.all(np.isneginf(lg[0, 1, :128]))
     fin = np.isfinite(l_ref)
-    assert np.max(np.abs(lg[fin] - l_ref[fin])) < TOL_LSE["bf16"]
+    assert np.max(np.abs(lg[fin] - l_ref[fin])) < TOL_LSE[w.dtype]
     assert torch.all(o1[0, 4 * 128:5 * 128, 0] == 0) and torch.all(o1[0, :128, 1] == 0)
+
+
+@pytest.mark.parametrize("page_size", [16, 128])
+def test_fp8_short_lists_batch2_paged(page_size):
+    """Rows that keep 1 to 6 blocks, with and without the diagonal, in two
+    sequences: the fp8 pipeline's start-up and clamped look-ahead loads."""
+    w = wl.Workload(f"fp8-short-lists-p{page_size}", 2, 128 * 12, 4, 2, 128, 128, "fp8", paged=True,
+                    page_size=page_size, sink=False, v_sigma=0.0, seed=21)
+    _announce(w.name)
+    inp = wl.make_inputs(w, device=DEV)
+    p = problem(w, inp)
+    nb = w.num_blocks
+    rng = np.random.default_rng(page_size)
+    m = np.zeros((w.batch, w.hq, nb, nb), dtype=bool)
+    for bi in range(w.batch):
+        for h in range(w.hq):
+            for i in range(nb):
+                cnt = int(rng.integers(1, min(i + 1, 6) + 1))
+                m[bi, h, i, rng.choice(i + 1, cnt, replace=False)] = True
+    m[1, 3, 7, :] = False                                     # and one empty row
+    words = torch.from_numpy(oracle.pack_block_mask(m).view(np.int32)).to(DEV)
+    o, lse = sb.attention(p, inp["q"], inp["k_pages"], inp["v_pages"], words, inp["block_table"], page_size)
+    oc, lc = sb.attention(p, inp["q"], inp["k"], inp["v"], words)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc) and torch.equal(lse, lc)
+    q, k, v = oracle_qkv(inp)
+    o_ref, l_ref = oracle.block_sparse_attention(q, k, v, m, w.block)
+    assert output_error(o, o_ref) < TOL_O["fp8"]
+    lg = lse.cpu().double().numpy()
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(lg), ~fin)
+    assert np.max(np.abs(lg[fin] - l_ref[fin])) < TOL_LSE["fp8"]
 
 
 def test_selection_special_values():
