@@ -95,6 +95,66 @@ def score_bytes(w: wl.Workload) -> float:
     return float(read + write)
 
 
+def cache_write_bytes(w: wl.Workload) -> float:
+    """Algorithmic HBM bytes of a KV-cache write: read the new K and V (bf16,
+    or fp32 for an fp32 cache), write them in the cache type, write kbar and
+    lvn."""
+    es_out = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    es_in = 4 if w.dtype == "f32" else 2
+    n = w.batch * w.seq * w.hkv * w.head_dim
+    return float(2 * n * (es_in + es_out) + 4 * w.batch * w.hkv * w.num_blocks * (w.head_dim + 1))
+
+
+def pooled_score_bytes(w: wl.Workload) -> float:
+    """Algorithmic HBM bytes of scoring from precomputed kbar/lvn: read Q,
+    kbar and lvn, write qbar and the score matrix."""
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    nb = w.num_blocks
+    read = w.batch * w.seq * w.hq * w.head_dim * es + 4 * w.batch * w.hkv * nb * (w.head_dim + 1)
+    write = 4 * w.batch * w.hq * nb * (w.head_dim + nb)
+    return float(read + write)
+
+
+def time_cache_write(w: wl.Workload, p, q, runs: int):
+    """The step before the path, timed on its own: the fused KV-cache write
+    (new bf16/fp32 K and V -> cache + kbar + lvn), then scoring from those
+    representations (Q pooled, score GEMM)."""
+    dev = "cuda"
+    src = wl.make_cache_inputs(w, device=dev, gen_device=dev)
+    pc = dataclasses.replace(p, k_scale=float(src["k_scale"]), v_scale=float(src["v_scale"]))
+    cdt = {"fp8": torch.float8_e4m3fn, "bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    if w.paged:
+        shape, table, page = (src["num_pages"], w.page_size, w.hkv, w.head_dim), src["block_table"], w.page_size
+    else:
+        shape, table, page = (w.batch, w.seq, w.hkv, w.head_dim), None, 0
+    kc = torch.empty(shape, dtype=cdt, device=dev)
+    vc = torch.empty_like(kc)
+    nb = w.num_blocks
+    kbar = torch.empty((w.batch, w.hkv, nb, w.head_dim), dtype=torch.float32, device=dev)
+    lvn = torch.empty((w.batch, w.hkv, nb), dtype=torch.float32, device=dev)
+    scores = torch.empty((w.batch, w.hq, nb, nb), dtype=torch.float32, device=dev)
+    ws = torch.empty(sb.stem_score_workspace_size(pc), dtype=torch.uint8, device=dev)
+    t_cw, t_sp = Timer(), Timer()
+    sb.stem_cache_write(pc, src["k"], src["v"], kc, vc, kbar, lvn, table, page)
+    sb.stem_score_pooled(pc, q, kbar, lvn, scores, ws)
+    for _ in range(runs):
+        with t_cw:
+            sb.stem_cache_write(pc, src["k"], src["v"], kc, vc, kbar, lvn, table, page)
+        with t_sp:
+            sb.stem_score_pooled(pc, q, kbar, lvn, scores, ws)
+    torch.cuda.synchronize()
+    cw_ms = sum(t_cw.ms()) / runs
+    sp_ms = sum(t_sp.ms()) / runs
+    del src, kc, vc, scores
+    return {
+        "cache_write_ms": cw_ms,
+        "cache_write_gbs": cache_write_bytes(w) / (cw_ms * 1e-3) / 1e9,
+        "cache_write_hbm_frac": cache_write_bytes(w) / (cw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "score_pooled_ms": sp_ms,
+        "score_pooled_gbs": pooled_score_bytes(w) / (sp_ms * 1e-3) / 1e9,
+    }
+
+
 class Timer:
     """HIP events on the stream the library launches on (torch's current stream)."""
 
@@ -175,6 +235,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cache-write", action="store_true",
+                    help="skip timing the fused KV-cache write and scoring from its output")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the attention source hash recorded next to measured traffic, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -305,6 +367,10 @@ def main():
         })
         log(f"[bench] dense {dense_ms:.3f} ms, density-1 sparse {full_ms:.3f} ms, "
             f"R {result['ratio_vs_dense']:.3f}")
+
+    if not args.no_cache_write:
+        log(f"[bench] fused KV-cache write and pooled scoring, {args.dense_steps} runs each")
+        result["before_the_path"] = time_cache_write(w, p, q, args.dense_steps)
 
     if not args.no_cpu_baseline:
         log("[bench] oracle CPU baseline (bounded sample)")

@@ -6,9 +6,10 @@ memory and the current HIP stream.  There is no fallback: if the library is
 missing, every call raises.
 
 Entry points mirror the C names:
-  stem_score_workspace_size, stem_score, stem_tpd_budget, stem_select,
-  bsa_prefill, stem_last_error
-plus allocating conveniences ``score``, ``select`` and ``attention``.
+  stem_score_workspace_size, stem_score, stem_score_sam, stem_score_pooled,
+  stem_cache_write, stem_tpd_budget, stem_select, bsa_prefill, stem_last_error
+plus allocating conveniences ``score``, ``score_pooled``, ``cache_write``,
+``select`` and ``attention``.
 """
 
 from __future__ import annotations
@@ -28,8 +29,9 @@ STEM_F32, STEM_BF16, STEM_FP8_E4M3 = 0, 1, 2
 _DTYPES = {"f32": STEM_F32, "bf16": STEM_BF16, "fp8": STEM_FP8_E4M3}
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
-EXPORTS = ("stem_score_workspace_size", "stem_score", "stem_tpd_budget", "stem_select",
-           "bsa_prefill", "stem_last_error")
+EXPORTS = ("stem_score_workspace_size", "stem_score", "stem_score_sam", "stem_score_pooled",
+           "stem_cache_write", "stem_tpd_budget", "stem_select", "bsa_prefill",
+           "stem_last_error")
 
 
 class StemError(RuntimeError):
@@ -67,6 +69,9 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, D, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
         h.stem_score_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
         h.stem_score.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, SZ, P]
+        h.stem_score_sam.argtypes = h.stem_score.argtypes
+        h.stem_score_pooled.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, SZ, P]
+        h.stem_cache_write.argtypes = [ctypes.POINTER(AttnDesc), P, P, ctypes.POINTER(KvDesc), P, P, P]
         h.stem_tpd_budget.argtypes = [I32, D, D, P, ctypes.POINTER(I64)]
         h.stem_select.argtypes = [ctypes.POINTER(AttnDesc), P, D, D, P, P, I32, P, P]
         h.bsa_prefill.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, P, P]
@@ -146,6 +151,30 @@ def stem_score(p: Problem, q, k, v, scores, workspace, block_table=None, page_si
                             _stream(stream)))
 
 
+def stem_score_sam(p: Problem, q, k, v, scores, workspace, block_table=None, page_size=0,
+                   stream=None):
+    d = p.desc()
+    kv = _kv(k, v, block_table, page_size)
+    _check(lib().stem_score_sam(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(scores),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)))
+
+
+def stem_score_pooled(p: Problem, q, kbar, lvn, scores, workspace, stream=None):
+    d = p.desc()
+    _check(lib().stem_score_pooled(ctypes.byref(d), _ptr(q), _ptr(kbar), _ptr(lvn), _ptr(scores),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
+
+
+def stem_cache_write(p: Problem, k_in, v_in, k_cache, v_cache, kbar, lvn, block_table=None,
+                     page_size=0, stream=None):
+    d = p.desc()
+    kv = _kv(k_cache, v_cache, block_table, page_size)
+    _check(lib().stem_cache_write(ctypes.byref(d), _ptr(k_in), _ptr(v_in), ctypes.byref(kv),
+                                  _ptr(kbar), _ptr(lvn), _stream(stream)))
+
+
 def stem_tpd_budget(num_blocks: int, density: float, alpha: float = 0.5):
     buf = (ctypes.c_int32 * max(num_blocks, 1))()
     total = ctypes.c_int64(0)
@@ -174,13 +203,34 @@ def stem_last_error() -> str:
 
 # ---- allocating conveniences -------------------------------------------------
 
-def score(p: Problem, q, k, v, block_table=None, page_size=0, stream=None):
-    """Returns (scores [b,Hq,Nb,Nb] fp32, workspace bytes as uint8)."""
+def score(p: Problem, q, k, v, block_table=None, page_size=0, stream=None, sam=False):
+    """Returns (scores [b,Hq,Nb,Nb] fp32, workspace bytes as uint8).  sam=True
+    leaves the value term out."""
     nb = p.num_blocks
     scores = torch.empty((p.batch, p.num_q_heads, nb, nb), dtype=torch.float32, device=q.device)
     ws = torch.empty(stem_score_workspace_size(p), dtype=torch.uint8, device=q.device)
-    stem_score(p, q, k, v, scores, ws, block_table, page_size, stream)
+    (stem_score_sam if sam else stem_score)(p, q, k, v, scores, ws, block_table, page_size, stream)
     return scores, ws
+
+
+def score_pooled(p: Problem, q, kbar, lvn=None, stream=None):
+    """Scores from precomputed kbar/lvn (lvn None: SAM).  Returns (scores, workspace)."""
+    nb = p.num_blocks
+    scores = torch.empty((p.batch, p.num_q_heads, nb, nb), dtype=torch.float32, device=q.device)
+    ws = torch.empty(stem_score_workspace_size(p), dtype=torch.uint8, device=q.device)
+    stem_score_pooled(p, q, kbar, lvn, scores, ws, stream)
+    return scores, ws
+
+
+def cache_write(p: Problem, k_in, v_in, k_cache, v_cache, block_table=None, page_size=0,
+                stream=None):
+    """Writes K/V into the given cache tensors; returns (kbar, lvn)."""
+    nb = p.num_blocks
+    dev = k_in.device
+    kbar = torch.empty((p.batch, p.num_kv_heads, nb, p.head_dim), dtype=torch.float32, device=dev)
+    lvn = torch.empty((p.batch, p.num_kv_heads, nb), dtype=torch.float32, device=dev)
+    stem_cache_write(p, k_in, v_in, k_cache, v_cache, kbar, lvn, block_table, page_size, stream)
+    return kbar, lvn
 
 
 def select(p: Problem, scores, density, alpha=0.5, with_list=False, stream=None):

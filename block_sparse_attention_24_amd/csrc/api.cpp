@@ -121,6 +121,31 @@ void workspace_layout(const Shape &s, size_t *qbar, size_t *kbar, size_t *lvn, s
     *total = *lvn + align256(nl);
 }
 
+// stem_score and stem_score_sam: pool Q, K (and V) into the workspace, then
+// the score GEMM (with the value term unless sam).
+int score_from_kv(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv, float *scores,
+                  void *workspace, size_t workspace_bytes, void *stream, bool sam) {
+    Shape s;
+    KvView v;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if ((rc = check_kv(kv, s, &v))) return rc;
+    if (!q || !scores || !workspace) return fail(STEM_EINVAL, "q, scores or workspace is NULL");
+    size_t oq, ok_, ol, total;
+    workspace_layout(s, &oq, &ok_, &ol, &total);
+    if (workspace_bytes < total)
+        return fail(STEM_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
+    if ((rc = hip_precheck())) return rc;
+    char *ws = static_cast<char *>(workspace);
+    float *qbar = reinterpret_cast<float *>(ws + oq);
+    float *kbar = reinterpret_cast<float *>(ws + ok_);
+    float *lvn = sam ? nullptr : reinterpret_cast<float *>(ws + ol);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_pool(s, q, &v, qbar, kbar, lvn, st);
+    if (e == hipSuccess) e = launch_score(s, qbar, kbar, lvn, scores, st);
+    return hip_status(e, sam ? "stem_score_sam launch" : "stem_score launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,25 +164,44 @@ int stem_score_workspace_size(const stem_attn_desc *desc, size_t *bytes) {
 
 int stem_score(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv, float *scores,
                void *workspace, size_t workspace_bytes, void *stream) {
+    return score_from_kv(desc, q, kv, scores, workspace, workspace_bytes, stream, false);
+}
+
+int stem_score_sam(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv, float *scores,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    return score_from_kv(desc, q, kv, scores, workspace, workspace_bytes, stream, true);
+}
+
+int stem_score_pooled(const stem_attn_desc *desc, const void *q, const float *kbar, const float *lvn,
+                      float *scores, void *workspace, size_t workspace_bytes, void *stream) {
     Shape s;
-    KvView v;
     int rc = check_desc(desc, &s);
     if (rc) return rc;
-    if ((rc = check_kv(kv, s, &v))) return rc;
-    if (!q || !scores || !workspace) return fail(STEM_EINVAL, "q, scores or workspace is NULL");
+    if (!q || !kbar || !scores || !workspace)
+        return fail(STEM_EINVAL, "q, kbar, scores or workspace is NULL");
     size_t oq, ok_, ol, total;
     workspace_layout(s, &oq, &ok_, &ol, &total);
     if (workspace_bytes < total)
         return fail(STEM_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
     if ((rc = hip_precheck())) return rc;
-    char *ws = static_cast<char *>(workspace);
-    float *qbar = reinterpret_cast<float *>(ws + oq);
-    float *kbar = reinterpret_cast<float *>(ws + ok_);
-    float *lvn = reinterpret_cast<float *>(ws + ol);
+    float *qbar = reinterpret_cast<float *>(static_cast<char *>(workspace) + oq);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_pool(s, q, v, qbar, kbar, lvn, st);
+    hipError_t e = launch_pool(s, q, nullptr, qbar, nullptr, nullptr, st);
     if (e == hipSuccess) e = launch_score(s, qbar, kbar, lvn, scores, st);
-    return hip_status(e, "stem_score launch");
+    return hip_status(e, "stem_score_pooled launch");
+}
+
+int stem_cache_write(const stem_attn_desc *desc, const void *k_in, const void *v_in,
+                     const stem_kv_desc *cache, float *kbar, float *lvn, void *stream) {
+    Shape s;
+    KvView v;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if ((rc = check_kv(cache, s, &v))) return rc;
+    if (!k_in || !v_in || !kbar || !lvn) return fail(STEM_EINVAL, "k_in, v_in, kbar or lvn is NULL");
+    if ((rc = hip_precheck())) return rc;
+    hipError_t e = launch_cache_write(s, k_in, v_in, v, kbar, lvn, static_cast<hipStream_t>(stream));
+    return hip_status(e, "stem_cache_write launch");
 }
 
 int stem_tpd_budget(int32_t num_blocks, double density, double alpha, int32_t *budget_host,

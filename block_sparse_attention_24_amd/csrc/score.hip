@@ -2,19 +2,27 @@
 // §二.2.1: compact block-level Q/K representations, then one GEMM gives every
 // block score, with no softmax, no gather and no token-level intermediate).
 //
-// Two kernels:
-//   pool_kernel   one HBM pass over Q, K, V: per block the mean of the Q rows
-//                 and of the K rows, and ln of the Frobenius norm of the V rows.
-//   score_kernel  per head, fp32 tiles of tau * qbar kbar^T + lvn on and below
-//                 the diagonal, -inf above it.
-// Both use a fixed summation order, so results are bit-reproducible.
+// Kernels:
+//   pool_kernel         one HBM pass over Q, K or V: per block the mean of the
+//                       rows, or ln of the Frobenius norm of the V rows.
+//   cache_write_kernel  the same block reductions fused into writing a
+//                       prefill's K and V into the (FP8, paged) cache: one pass
+//                       over the new tokens stores them and pools them.
+//   score_kernel        per head, tau * qbar kbar^T (+ lvn) on the matrix
+//                       cores, -inf above the diagonal.
+// All use a fixed summation order, so results are bit-reproducible; the cache
+// write accumulates exactly as pool_kernel does over the stored values, so
+// its representations equal, bit for bit, those pooled later from the cache.
 #include "device_common.h"
 #include "stem_internal.h"
 
 namespace stem {
 namespace {
 
+// Pooling workgroups: 64 column chunks x 4 row groups (one wave each).
 constexpr int kPoolThreads = 256;
+constexpr int kPoolChunks = 64;
+constexpr int kRowGroups = kPoolThreads / kPoolChunks;
 
 struct PoolArgs {
     const char *base;          // Q, K or V
@@ -26,13 +34,90 @@ struct PoolArgs {
     float scale;               // dequantisation scale
 };
 
-// Thread = one 16-byte column chunk of a token row; a workgroup covers 256
-// chunks of one block and walks its blk rows in order.  MODE 0: mean of the
-// rows; MODE 1: sum of squares, reduced over each head's chunks -> lvn.
+// Row of token tok of sequence b in a contiguous or paged [rows, H, d] tensor.
+__device__ __forceinline__ size_t token_row(const int32_t *table, int page_log2, int pages_per_seq,
+                                            int seq, int b, int tok) {
+    if (table) {
+        const int page = table[(size_t)b * pages_per_seq + (tok >> page_log2)];
+        return ((size_t)page << page_log2) + (tok & ((1 << page_log2) - 1));
+    }
+    return (size_t)b * seq + tok;
+}
+
+// Block reductions, shared by pool_kernel and cache_write_kernel so that both
+// produce the same bits.  A thread owns EPC consecutive elements (one 16-byte
+// chunk of the stored row) and sees its row group's rows in order.
+//   MODE 0: acc = sum of the rows; out = acc / blk * scale (the mean).
+//   MODE 1: acc = sum of squares; the chunks of one head are reduced by a
+//           butterfly and out = ln(sqrt(sum)) + ln(scale).
+template <int EPC, int MODE>
+__device__ __forceinline__ void pool_add(float *acc, const float *x) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+        if constexpr (MODE == 0) acc[e] += x[e];
+        else acc[e] = fmaf(x[e], x[e], acc[e]);
+    }
+}
+
+template <int EPC, int MODE>
+__device__ __forceinline__ void pool_store(const float *acc, bool active, int chunk, float *out,
+                                           int b, int heads, int nb, int d, int blk_j, int blk,
+                                           float scale) {
+    const int col = chunk * EPC;              // first element (head-major, then d)
+    const int h = col / d;
+    const int dd = col % d;
+    if constexpr (MODE == 0) {
+        if (!active) return;
+        const float f = 1.0f / (float)blk;
+        float *dst = out + (((size_t)b * heads + h) * nb + blk_j) * d + dd;
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+            f32x4 v;
+            v[0] = acc[e] * f * scale;
+            v[1] = acc[e + 1] * f * scale;
+            v[2] = acc[e + 2] * f * scale;
+            v[3] = acc[e + 3] * f * scale;
+            *reinterpret_cast<f32x4 *>(dst + e) = v;
+        }
+    } else {
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s += acc[e];
+        // butterfly over the chunks of one head (a power of two <= 32, aligned)
+        const int cph = d / EPC;
+        for (int off = 1; off < cph; off <<= 1) s += __shfl_xor(s, off);
+        if (active && (chunk % cph) == 0)
+            out[((size_t)b * heads + h) * nb + blk_j] = 0.5f * logf(s) + logf(scale);
+    }
+}
+
+// Row groups: wave w accumulates rows [w blk/4, (w+1) blk/4) of the block in
+// order; the other waves' partial sums are then added to wave 0's in wave
+// order through LDS (part: (kRowGroups - 1) * EPC * 64 floats).  Returns true
+// in wave 0, which holds the block's sums.
+template <int EPC>
+__device__ __forceinline__ bool combine_row_groups(float *acc, float *part) {
+    const int lane = threadIdx.x % kPoolChunks, wave = threadIdx.x / kPoolChunks;
+    if (wave) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) part[((wave - 1) * EPC + e) * kPoolChunks + lane] = acc[e];
+    }
+    __syncthreads();
+    if (wave) return false;
+#pragma unroll
+    for (int g = 0; g < kRowGroups - 1; ++g)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += part[(g * EPC + e) * kPoolChunks + lane];
+    return true;
+}
+
+// Thread = one 16-byte column chunk of a token row in one row group.
 template <int ES, int MODE>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
     constexpr int EPC = 16 / ES;              // elements per chunk
-    const int chunk = blockIdx.x * kPoolThreads + threadIdx.x;
+    __shared__ float part[(kRowGroups - 1) * EPC * kPoolChunks];
+    const int chunk = blockIdx.x * kPoolChunks + threadIdx.x % kPoolChunks;
+    const int group = threadIdx.x / kPoolChunks;
     const int blk_j = blockIdx.y;
     const int b = blockIdx.z;
     const bool active = chunk < a.chunks_per_row;
@@ -43,183 +128,255 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
     for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
 
     if (active) {
-        const int tok0 = blk_j * a.blk;
+        const int rows = a.blk / kRowGroups;
+        const int tok0 = blk_j * a.blk + group * rows;
 #pragma unroll 8
-        for (int t = 0; t < a.blk; ++t) {
-            const int tok = tok0 + t;
-            size_t row;
-            if (a.table) {
-                const int page = a.table[(size_t)b * a.pages_per_seq + (tok >> a.page_log2)];
-                row = ((size_t)page << a.page_log2) + (tok & ((1 << a.page_log2) - 1));
-            } else {
-                row = (size_t)b * a.seq + tok;
-            }
+        for (int t = 0; t < rows; ++t) {
+            const size_t row = token_row(a.table, a.page_log2, a.pages_per_seq, a.seq, b, tok0 + t);
             const uint4 u = *reinterpret_cast<const uint4 *>(a.base + row * row_bytes + (size_t)chunk * 16);
             float x[EPC];
             widen16<ES>(u, x);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                if constexpr (MODE == 0) acc[e] += x[e];
-                else acc[e] = fmaf(x[e], x[e], acc[e]);
-            }
+            pool_add<EPC, MODE>(acc, x);
         }
     }
+    if (combine_row_groups<EPC>(acc, part))
+        pool_store<EPC, MODE>(acc, active, chunk, a.out, b, a.heads, a.nb, a.d, blk_j, a.blk, a.scale);
+}
 
-    const int col = chunk * EPC;              // first element (head-major, then d)
-    const int h = col / a.d;
-    const int dd = col % a.d;
-    if constexpr (MODE == 0) {
-        if (!active) return;
-        const float f = 1.0f / (float)a.blk;
-        float *dst = a.out + (((size_t)b * a.heads + h) * a.nb + blk_j) * a.d + dd;
+// ---------------------------------------------------------------------------
+// Cache write with the K/V block reductions fused in.
+// ---------------------------------------------------------------------------
+struct CacheArgs {
+    const char *src[2];        // new K, V: [b, S, Hkv, d] in the input type
+    char *dst[2];              // cache K, V: contiguous or paged, in the cache type
+    float *kbar, *lvn;
+    const int32_t *table;
+    int page_log2, pages_per_seq;
+    int heads, d, blk, seq, nb;
+    int chunks_per_row;        // 16-byte chunks of one cached token row
+    float scale[2];            // K and V quantisation scales (1 unless FP8)
+};
+
+// Nearest OCP E4M3 codes of x / scale for 16 values, ties to even, saturating
+// at +-448 (the conversion instruction rounds to nearest even; the clamp makes
+// out-of-range values saturate instead of overflowing).
+__device__ __forceinline__ uint4 quantize16_e4m3(const float *x, float scale) {
+    uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < EPC; e += 4) {
-            f32x4 v;
-            v[0] = acc[e] * f * a.scale;
-            v[1] = acc[e + 1] * f * a.scale;
-            v[2] = acc[e + 2] * f * a.scale;
-            v[3] = acc[e + 3] * f * a.scale;
-            *reinterpret_cast<f32x4 *>(dst + e) = v;
-        }
-    } else {
-        float s = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+        float q[4];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) s += acc[e];
-        // butterfly over the chunks of one head (a power of two <= 32, aligned)
-        const int cph = a.d / EPC;
-        for (int off = 1; off < cph; off <<= 1) s += __shfl_xor(s, off);
-        if (active && (chunk % cph) == 0)
-            a.out[((size_t)b * a.heads + h) * a.nb + blk_j] = 0.5f * logf(s) + logf(a.scale);
+        for (int e = 0; e < 4; ++e) q[e] = fminf(fmaxf(x[4 * i + e] / scale, -448.0f), 448.0f);
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
+        w[i] = (uint32_t)p;
     }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Thread = one 16-byte chunk of the cached row (EPC = 16 / ES_OUT elements,
+// read from EPC * ES_IN input bytes); blockIdx.z = 2 * b + (0: K, 1: V).
+template <int ES_IN, int ES_OUT, int MODE>
+__device__ __forceinline__ void cache_write_body(const CacheArgs &a, int b, float *part) {
+    constexpr int EPC = 16 / ES_OUT;
+    constexpr int IN_VEC = EPC * ES_IN / 16;  // 16-byte input loads per chunk
+    const int chunk = blockIdx.x * kPoolChunks + threadIdx.x % kPoolChunks;
+    const int group = threadIdx.x / kPoolChunks;
+    const int blk_j = blockIdx.y;
+    const bool active = chunk < a.chunks_per_row;
+    const size_t out_row_bytes = (size_t)a.chunks_per_row * 16;
+    const size_t in_row_bytes = out_row_bytes * ES_IN / ES_OUT;
+    const char *src = a.src[MODE];
+    char *dst = a.dst[MODE];
+    const float scale = a.scale[MODE];
+
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+
+    if (active) {
+        const int rows = a.blk / kRowGroups;
+        const int tok0 = blk_j * a.blk + group * rows;
+#pragma unroll 4
+        for (int t = 0; t < rows; ++t) {
+            const int tok = tok0 + t;
+            const char *in = src + ((size_t)b * a.seq + tok) * in_row_bytes + (size_t)chunk * 16 * IN_VEC;
+            uint4 stored;
+            if constexpr (ES_OUT == 1) {
+                float x[EPC];
+#pragma unroll
+                for (int i = 0; i < IN_VEC; ++i)
+                    widen16<ES_IN>(reinterpret_cast<const uint4 *>(in)[i], x + i * (16 / ES_IN));
+                stored = quantize16_e4m3(x, scale);
+            } else {
+                stored = *reinterpret_cast<const uint4 *>(in);   // same type: a copy
+            }
+            const size_t row = token_row(a.table, a.page_log2, a.pages_per_seq, a.seq, b, tok);
+            *reinterpret_cast<uint4 *>(dst + row * out_row_bytes + (size_t)chunk * 16) = stored;
+            float x[EPC];
+            widen16<ES_OUT>(stored, x);       // exactly what pool_kernel reads back
+            pool_add<EPC, MODE>(acc, x);
+        }
+    }
+    if (combine_row_groups<EPC>(acc, part))
+        pool_store<EPC, MODE>(acc, active, chunk, MODE == 0 ? a.kbar : a.lvn, b, a.heads, a.nb, a.d,
+                              blk_j, a.blk, scale);
+}
+
+template <int ES_IN, int ES_OUT>
+__global__ __launch_bounds__(kPoolThreads) void cache_write_kernel(CacheArgs a) {
+    __shared__ float part[(kRowGroups - 1) * (16 / ES_OUT) * kPoolChunks];
+    const int b = blockIdx.z >> 1;
+    if (blockIdx.z & 1) cache_write_body<ES_IN, ES_OUT, 1>(a, b, part);
+    else cache_write_body<ES_IN, ES_OUT, 0>(a, b, part);
 }
 
 template <int ES>
-hipError_t pool_all(const Shape &s, const void *q, const KvView &kv, float *qbar, float *kbar,
-                    float *lvn, hipStream_t st) {
+hipError_t pool_one(const Shape &s, const void *base, const int32_t *table, int page_log2,
+                    int pages_per_seq, int heads, float scale, float *out, int mode, hipStream_t st) {
     PoolArgs a{};
+    a.base = static_cast<const char *>(base);
+    a.out = out;
+    a.table = table;
+    a.page_log2 = page_log2;
+    a.pages_per_seq = pages_per_seq;
+    a.heads = heads;
     a.d = s.d;
     a.blk = s.blk;
     a.seq = s.seq;
     a.nb = s.nb;
-    // Q: always contiguous
-    a.base = static_cast<const char *>(q);
-    a.out = qbar;
-    a.table = nullptr;
-    a.heads = s.hq;
-    a.chunks_per_row = s.hq * s.d * ES / 16;
-    a.scale = s.q_scale;
-    dim3 grid((a.chunks_per_row + kPoolThreads - 1) / kPoolThreads, s.nb, s.batch);
-    hipLaunchKernelGGL((pool_kernel<ES, 0>), grid, dim3(kPoolThreads), 0, st, a);
-    // K and V: contiguous or paged
-    a.table = kv.table;
-    a.page_log2 = kv.page_log2;
-    a.pages_per_seq = kv.pages_per_seq;
-    a.heads = s.hkv;
-    a.chunks_per_row = s.hkv * s.d * ES / 16;
-    grid.x = (a.chunks_per_row + kPoolThreads - 1) / kPoolThreads;
-    a.base = static_cast<const char *>(kv.k);
-    a.out = kbar;
-    a.scale = s.k_scale;
-    hipLaunchKernelGGL((pool_kernel<ES, 0>), grid, dim3(kPoolThreads), 0, st, a);
-    a.base = static_cast<const char *>(kv.v);
-    a.out = lvn;
-    a.scale = s.v_scale;
-    hipLaunchKernelGGL((pool_kernel<ES, 1>), grid, dim3(kPoolThreads), 0, st, a);
+    a.chunks_per_row = heads * s.d * ES / 16;
+    a.scale = scale;
+    dim3 grid((a.chunks_per_row + kPoolChunks - 1) / kPoolChunks, s.nb, s.batch);
+    if (mode == 0) hipLaunchKernelGGL((pool_kernel<ES, 0>), grid, dim3(kPoolThreads), 0, st, a);
+    else hipLaunchKernelGGL((pool_kernel<ES, 1>), grid, dim3(kPoolThreads), 0, st, a);
     return hipGetLastError();
 }
 
+template <int ES>
+hipError_t pool_all(const Shape &s, const void *q, const KvView *kv, float *qbar, float *kbar,
+                    float *lvn, hipStream_t st) {
+    hipError_t e = pool_one<ES>(s, q, nullptr, 0, 0, s.hq, s.q_scale, qbar, 0, st);
+    if (e != hipSuccess || !kv) return e;
+    e = pool_one<ES>(s, kv->k, kv->table, kv->page_log2, kv->pages_per_seq, s.hkv, s.k_scale, kbar, 0, st);
+    if (e != hipSuccess || !lvn) return e;
+    return pool_one<ES>(s, kv->v, kv->table, kv->page_log2, kv->pages_per_seq, s.hkv, s.v_scale, lvn, 1, st);
+}
+
 // ---------------------------------------------------------------------------
-// Score GEMM: a 64 x 64 tile of (I, J) per workgroup, 4 x 4 outputs per
-// thread, d streamed through LDS in slices of 32 (stored d-major so a thread
-// reads its four rows as one 16-byte word).
+// Score GEMM on the matrix cores (v_mfma_f32_32x32x2f32, fp32 in and out).  A
+// workgroup owns a 128 x 128 tile of (I, J), each of its four waves a 64 x 64
+// quarter held as 2 x 2 MFMA tiles.  Per chunk of 8 dimensions a lane loads
+// four consecutive floats of one qbar row and of one kbar row straight from
+// global memory (lanes 0-31 dimensions d0..d0+3, lanes 32-63 d0+4..d0+7), so
+// MFMA step c of the chunk pairs dimension d0+c with d0+4+c.  The order of
+// the sum is fixed, so the scores are bit-reproducible.  Workgroups are
+// renumbered so that each XCD (workgroup id mod 8) takes a contiguous eighth
+// of the heads and reads their representations into its own L2.
 // ---------------------------------------------------------------------------
-constexpr int kTile = 64;
-constexpr int kSlice = 32;
+constexpr int kTile = 128;
 
 struct ScoreArgs {
-    const float *qbar, *kbar, *lvn;
+    const float *qbar, *kbar, *lvn;   // lvn == nullptr: no value term (SAM)
     float *scores;
-    int hq, hkv, nb, d;
+    int hq, hkv, nb, tiles;
     float tau;
 };
 
+template <int D>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-    __shared__ float qs[kSlice][kTile + 4];
-    __shared__ float ks[kSlice][kTile + 4];
-    const int tiles = (a.nb + kTile - 1) / kTile;
-    const int ti = blockIdx.x / tiles;          // I tile
-    const int tj = blockIdx.x % tiles;          // J tile
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
+    // XCD-contiguous renumbering of (tile, head, batch)
+    const unsigned n = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const unsigned total = gridDim.x * gridDim.y * gridDim.z;
+    const unsigned m = (total & 7u) ? n : (n & 7u) * (total >> 3) + (n >> 3);
+    const int tile = (int)(m % gridDim.x);
+    const int h = (int)((m / gridDim.x) % gridDim.y);
+    const int b = (int)(m / (gridDim.x * gridDim.y));
+    const int ti = tile / a.tiles, tj = tile % a.tiles;
     const int g = h / (a.hq / a.hkv);
     const int tid = threadIdx.x;
-    const int r0 = (tid / 16) * 4;              // 4 rows (I) of this thread
-    const int c0 = (tid % 16) * 4;              // 4 cols (J)
-    float *out = a.scores + (((size_t)b * a.hq + h) * a.nb) * a.nb;
+    float *out = a.scores + ((size_t)b * a.hq + h) * a.nb * a.nb;
     const float ninf = -__builtin_huge_valf();
 
-    if (tj > ti) {                              // wholly above the diagonal
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int I = ti * kTile + r0 + r;
-            if (I >= a.nb) continue;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int J = tj * kTile + c0 + c;
-                if (J < a.nb) out[(size_t)I * a.nb + J] = ninf;
-            }
+    const int w = tid >> 6, lane = tid & 63;
+    const int r = lane & 31, kh = lane >> 5;
+    const int I0 = ti * kTile + (w >> 1) * 64;
+    const int J0 = tj * kTile + (w & 1) * 64;
+    if (I0 >= a.nb || J0 >= a.nb) return;      // nothing of this quarter is stored
+
+    if (J0 > I0 + 63) {               // this quarter lies wholly above the diagonal
+        for (int i = 0; i < 64; ++i) {
+            const int I = I0 + i;
+            if (I >= a.nb) break;
+            if (J0 + lane < a.nb) out[(size_t)I * a.nb + J0 + lane] = ninf;
         }
         return;
     }
 
-    const float *qb = a.qbar + (((size_t)b * a.hq + h) * a.nb) * a.d;
-    const float *kb = a.kbar + (((size_t)b * a.hkv + g) * a.nb) * a.d;
-    float acc[4][4];
+    const float *qb = a.qbar + ((size_t)b * a.hq + h) * a.nb * D + 4 * kh;
+    const float *kb = a.kbar + ((size_t)b * a.hkv + g) * a.nb * D + 4 * kh;
+    const float *qr[2], *kr[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
-
-    for (int d0 = 0; d0 < a.d; d0 += kSlice) {
-        // 64 rows x 32 d of each operand: 2048 floats, 8 per thread
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = tid + 256 * i;
-            const int row = e / kSlice, dd = e % kSlice;
-            const int I = ti * kTile + row, J = tj * kTile + row;
-            qs[dd][row] = I < a.nb ? qb[(size_t)I * a.d + d0 + dd] : 0.0f;
-            ks[dd][row] = J < a.nb ? kb[(size_t)J * a.d + d0 + dd] : 0.0f;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int dd = 0; dd < kSlice; ++dd) {
-            const f32x4 qv = *reinterpret_cast<const f32x4 *>(&qs[dd][r0]);
-            const f32x4 kv = *reinterpret_cast<const f32x4 *>(&ks[dd][c0]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(qv[r], kv[c], acc[r][c]);
-        }
-        __syncthreads();
+    for (int i = 0; i < 2; ++i) {     // rows past the end read the last row; never stored
+        qr[i] = qb + (size_t)min(I0 + 32 * i + r, a.nb - 1) * D;
+        kr[i] = kb + (size_t)min(J0 + 32 * i + r, a.nb - 1) * D;
     }
 
-    const float *lv = a.lvn + ((size_t)b * a.hkv + g) * a.nb;
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int I = ti * kTile + r0 + r;
-        if (I >= a.nb) continue;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int J = tj * kTile + c0 + c;
-            if (J >= a.nb) continue;
-            out[(size_t)I * a.nb + J] = J <= I ? fmaf(acc[r][c], a.tau, lv[J]) : ninf;
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    // three-deep ring: chunk n + 2 is requested before chunk n is multiplied
+    constexpr int NC = D / 8;
+    f32x4 A[3][2], B[3][2];
+    auto load = [&](int n) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            A[n % 3][i] = *reinterpret_cast<const f32x4 *>(qr[i] + 8 * n);
+            B[n % 3][i] = *reinterpret_cast<const f32x4 *>(kr[i] + 8 * n);
         }
+    };
+    load(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        if (n + 2 < NC) load(n + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[n % 3][i][c], B[n % 3][j][c],
+                                                                     acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // lane holds column J0 + 32 j + r and rows I0 + 32 i + 8 (v / 4) + 4 kh + v % 4
+    const float *lv = a.lvn ? a.lvn + ((size_t)b * a.hkv + g) * a.nb : nullptr;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int J = J0 + 32 * j + r;
+        if (J >= a.nb) continue;
+        const float lj = lv ? lv[J] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int I = I0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
+                if (I < a.nb) out[(size_t)I * a.nb + J] = J <= I ? fmaf(acc[i][j][v], a.tau, lj) : ninf;
+            }
     }
 }
 
 }  // namespace
 
-hipError_t launch_pool(const Shape &s, const void *q, const KvView &kv, float *qbar, float *kbar,
+hipError_t launch_pool(const Shape &s, const void *q, const KvView *kv, float *qbar, float *kbar,
                        float *lvn, hipStream_t st) {
     switch (s.dtype) {
         case STEM_F32: return pool_all<4>(s, q, kv, qbar, kbar, lvn, st);
@@ -230,9 +387,41 @@ hipError_t launch_pool(const Shape &s, const void *q, const KvView &kv, float *q
 
 hipError_t launch_score(const Shape &s, const float *qbar, const float *kbar, const float *lvn,
                         float *scores, hipStream_t st) {
-    ScoreArgs a{qbar, kbar, lvn, scores, s.hq, s.hkv, s.nb, s.d, s.tau};
     const int tiles = (s.nb + kTile - 1) / kTile;
-    hipLaunchKernelGGL(score_kernel, dim3(tiles * tiles, s.hq, s.batch), dim3(256), 0, st, a);
+    ScoreArgs a{qbar, kbar, lvn, scores, s.hq, s.hkv, s.nb, tiles, s.tau};
+    const dim3 grid(tiles * tiles, s.hq, s.batch);
+    if (s.d == 64) hipLaunchKernelGGL(score_kernel<64>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(score_kernel<128>, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_write(const Shape &s, const void *k_in, const void *v_in, const KvView &cache,
+                              float *kbar, float *lvn, hipStream_t st) {
+    CacheArgs a{};
+    a.src[0] = static_cast<const char *>(k_in);
+    a.src[1] = static_cast<const char *>(v_in);
+    a.dst[0] = static_cast<char *>(const_cast<void *>(cache.k));
+    a.dst[1] = static_cast<char *>(const_cast<void *>(cache.v));
+    a.kbar = kbar;
+    a.lvn = lvn;
+    a.table = cache.table;
+    a.page_log2 = cache.page_log2;
+    a.pages_per_seq = cache.pages_per_seq;
+    a.heads = s.hkv;
+    a.d = s.d;
+    a.blk = s.blk;
+    a.seq = s.seq;
+    a.nb = s.nb;
+    a.scale[0] = s.k_scale;
+    a.scale[1] = s.v_scale;
+    const int es = s.dtype == STEM_F32 ? 4 : s.dtype == STEM_BF16 ? 2 : 1;
+    a.chunks_per_row = s.hkv * s.d * es / 16;
+    const dim3 grid((a.chunks_per_row + kPoolChunks - 1) / kPoolChunks, s.nb, 2 * s.batch);
+    switch (s.dtype) {
+        case STEM_F32: hipLaunchKernelGGL((cache_write_kernel<4, 4>), grid, dim3(kPoolThreads), 0, st, a); break;
+        case STEM_BF16: hipLaunchKernelGGL((cache_write_kernel<2, 2>), grid, dim3(kPoolThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL((cache_write_kernel<2, 1>), grid, dim3(kPoolThreads), 0, st, a); break;
+    }
     return hipGetLastError();
 }
 

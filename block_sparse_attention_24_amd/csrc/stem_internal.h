@@ -76,10 +76,14 @@ __host__ __device__ inline int tpd_row_budget(const TpdPlan &p, int row) {
 int tpd_make_plan(int nb, double density, double alpha, TpdPlan *out, const char **why);
 
 // Launchers (enqueue only; return the launch status).
-hipError_t launch_pool(const Shape &s, const void *q, const KvView &kv,
+// launch_pool: Q always; K when kv is given; V when kv and lvn are given.
+hipError_t launch_pool(const Shape &s, const void *q, const KvView *kv,
                        float *qbar, float *kbar, float *lvn, hipStream_t st);
+// launch_score: lvn == nullptr leaves the value term out (SAM).
 hipError_t launch_score(const Shape &s, const float *qbar, const float *kbar, const float *lvn,
                         float *scores, hipStream_t st);
+hipError_t launch_cache_write(const Shape &s, const void *k_in, const void *v_in,
+                              const KvView &cache, float *kbar, float *lvn, hipStream_t st);
 hipError_t launch_select(const Shape &s, const TpdPlan &plan, const float *scores,
                          uint32_t *mask, int32_t *list, int list_stride, int32_t *count,
                          hipStream_t st);

@@ -16,6 +16,17 @@
  *                §二.3 "operator benchmark".
  * stem_tpd_budget exposes the budget on the host.
  *
+ * Around the path:
+ *   stem_score_sam     the score-only metric (SAM) that OAM is contrasted
+ *                      with (setupai.cc summary, "Technical Deep Dive"): the
+ *                      same scores without the value term, for ablations.
+ *   stem_cache_write   writes a prefill's K and V into the (FP8, paged) cache
+ *                      and computes the key-block means and value-block norms
+ *                      in the same pass, so scoring does not read K and V
+ *                      again (cn486.com article, §二.2.1: precomputed compact
+ *                      block representations; §二.2.2: paged FP8 KV in vLLM).
+ *   stem_score_pooled  scoring from those precomputed representations.
+ *
  * Conventions for every entry point
  *   - Tensors are row-major, in caller-owned DEVICE memory unless a comment
  *     says "host".  The library never allocates or frees memory and never
@@ -106,6 +117,48 @@ int stem_score_workspace_size(const stem_attn_desc *desc, size_t *bytes);
  * workspace: device memory of at least stem_score_workspace_size() bytes. */
 int stem_score(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
                float *scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/* SAM block scores: stem_score without the value term (the score-only
+ * metric the setupai.cc summary, "Technical Deep Dive", contrasts OAM with):
+ *   scores[b, h, I, J] = tau * <qbar[b,h,I], kbar[b,g(h),J]>   for J <= I, -inf above.
+ * Arguments, workspace and errors as stem_score; the lvn region of the
+ * workspace is left unwritten. */
+int stem_score_sam(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                   float *scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Block scores from key-block representations computed earlier (by
+ * stem_cache_write, or left in a stem_score workspace): pools Q into the qbar
+ * region of the workspace, then the score GEMM of stem_score.
+ *   kbar: fp32 [batch, num_kv_heads, Nb, head_dim], dequantised means.
+ *   lvn:  fp32 [batch, num_kv_heads, Nb], or NULL for SAM scores.
+ *   workspace: at least stem_score_workspace_size() bytes (only qbar is written).
+ * Given the kbar and lvn stem_score would pool from the same K/V, the scores
+ * are bit-identical to stem_score's. */
+int stem_score_pooled(const stem_attn_desc *desc, const void *q, const float *kbar,
+                      const float *lvn, float *scores, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Writes one prefill's keys and values into the KV cache and, in the same
+ * pass over the new tokens, the block representations scoring needs (Stem
+ * article on cn486.com, §二.2.1 and §二.2.2).
+ *   desc:  shape; desc->dtype is the CACHE's element type.
+ *          STEM_FP8_E4M3: k_in and v_in are bf16; each element x is stored
+ *          as the E4M3 code nearest to the fp32 quotient x / scale (ties to
+ *          even, saturating at +-448), scale = desc->k_scale or v_scale.
+ *          Inputs must be finite.
+ *          STEM_BF16, STEM_F32: k_in and v_in have that type and are copied.
+ *   k_in, v_in: [batch, seq_len, num_kv_heads, head_dim] (contiguous).
+ *   cache: the destination, contiguous or paged exactly as stem_kv_desc
+ *          describes for reading; cache->k and cache->v are WRITTEN.  Pages
+ *          of different tokens must not alias.
+ *   kbar:  fp32 [batch, num_kv_heads, Nb, head_dim], mean of each block's
+ *          stored (dequantised) key rows.
+ *   lvn:   fp32 [batch, num_kv_heads, Nb], ln of the Frobenius norm of each
+ *          block's stored (dequantised) value rows.
+ * kbar and lvn are bit-identical to what stem_score pools from the written
+ * cache, so stem_score_pooled with them gives stem_score's scores. */
+int stem_cache_write(const stem_attn_desc *desc, const void *k_in, const void *v_in,
+                     const stem_kv_desc *cache, float *kbar, float *lvn, void *stream);
 
 /* TPD budget on the host (Stem article §一.3.1; setupai.cc "Technical Deep
  * Dive").  T = floor(density * Nb(Nb+1)/2 + 1/2) computed in double, clamped

@@ -24,6 +24,7 @@ from .stem import (  # noqa: F401
     E4M3_MAX,
     attention_rows,
     block_sparse_attention,
+    cache_write,
     causal_block_count,
     dense_causal_attention,
     dequantize,
@@ -31,6 +32,8 @@ from .stem import (  # noqa: F401
     oam_scores,
     pack_block_mask,
     pool_blocks,
+    quantize_e4m3,
+    sam_scores,
     select_blocks,
     select_row,
     stem_pipeline,

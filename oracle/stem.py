@@ -121,6 +121,66 @@ def oam_scores(q, k, v, block, softmax_scale=None):
     return s
 
 
+def sam_scores(q, k, block, softmax_scale=None):
+    """Score-only block scores (SAM, the metric Stem-en's Deep Dive contrasts
+    OAM with: attention scores alone, no value information):
+    s[b, h, I, J] = tau * <qbar_hI, kbar_gJ> for J <= I, -inf above."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    b, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    nb = S // block
+    qbar = q.reshape(b, nb, block, Hq, d).mean(axis=2)          # [b, Nb, Hq, d]
+    kbar = k.reshape(b, nb, block, Hkv, d).mean(axis=2)         # [b, Nb, Hkv, d]
+    group = Hq // Hkv
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    s = np.full((b, Hq, nb, nb), -np.inf)
+    for bi in range(b):
+        for h in range(Hq):
+            logits = tau * (qbar[bi, :, h, :] @ kbar[bi, :, h // group, :].T)
+            for i in range(nb):
+                s[bi, h, i, :i + 1] = logits[i, :i + 1]
+    return s
+
+
+# --------------------------------------------------------------------------
+# KV-cache write  [Stem-cn §二.2.1 compact block representations computed
+# ahead of scoring; §二.2.2 FP8 paged KV]
+# --------------------------------------------------------------------------
+
+def quantize_e4m3(x, scale):
+    """E4M3 value stored for x under a per-tensor scale: the single-precision
+    quotient x / scale (IEEE division, the precision the write computes in),
+    then the nearest E4M3 value, ties to even, saturating at +-448.  Returns
+    the stored values (not multiplied back by the scale) in fp64."""
+    quotient = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    return e4m3fn_round(quotient.astype(np.float64))
+
+
+def cache_write(k, v, block, fp8=False, k_scale=1.0, v_scale=1.0):
+    """What a prefill's cache write stores and the block representations of
+    the stored values.  k, v: [b, S, Hkv, d].
+    Returns (k_stored, v_stored, kbar, lvn): the stored element values
+    (E4M3 values when fp8, else the inputs), and kbar [b, Hkv, Nb, d] / lvn
+    [b, Hkv, Nb] of the dequantised stored values (as pool_blocks defines
+    them)."""
+    if fp8:
+        ks = quantize_e4m3(k, k_scale)
+        vs = quantize_e4m3(v, v_scale)
+    else:
+        ks = np.asarray(k, dtype=np.float64)
+        vs = np.asarray(v, dtype=np.float64)
+        k_scale = v_scale = 1.0
+    kd, vd = dequantize(ks, k_scale), dequantize(vs, v_scale)
+    b, S, Hkv, d = kd.shape
+    nb = S // block
+    kbar = kd.reshape(b, nb, block, Hkv, d).mean(axis=2).transpose(0, 2, 1, 3)
+    sq = (vd.reshape(b, nb, block, Hkv, d) ** 2).sum(axis=(2, 4))
+    with np.errstate(divide="ignore"):
+        lvn = 0.5 * np.log(sq).transpose(0, 2, 1)
+    return ks, vs, kbar, lvn
+
+
 # --------------------------------------------------------------------------
 # TPD budget  [Stem-cn §一.3.1; Stem-en Technical Deep Dive]
 # --------------------------------------------------------------------------

@@ -61,6 +61,10 @@ def test_bad_shapes_rejected_everywhere(kw, code):
     assert sb.lib().stem_select(ctypes.byref(d), FAKE, 0.25, 0.5, FAKE, None, 0, None, None) == code
     kv = sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
     assert sb.lib().bsa_prefill(ctypes.byref(d), FAKE, ctypes.byref(kv), None, FAKE, None, None) == code
+    L = sb.lib()
+    assert L.stem_score_sam(ctypes.byref(d), FAKE, ctypes.byref(kv), FAKE, FAKE, 1 << 30, None) == code
+    assert L.stem_score_pooled(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == code
+    assert L.stem_cache_write(ctypes.byref(d), FAKE, FAKE, ctypes.byref(kv), FAKE, FAKE, None) == code
     assert sb.stem_last_error() != ""
 
 
@@ -84,6 +88,27 @@ def test_null_pointers_rejected():
     kv = sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
     assert sb.lib().bsa_prefill(ctypes.byref(d), None, ctypes.byref(kv), None, FAKE, None, None) == sb.STEM_EINVAL
     assert sb.lib().bsa_prefill(ctypes.byref(d), FAKE, ctypes.byref(kv), None, None, None, None) == sb.STEM_EINVAL
+
+
+def test_new_entry_points_reject_nulls_and_small_workspace():
+    d = _desc()
+    L = sb.lib()
+    kv = sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
+    n = sb.stem_score_workspace_size(sb.Problem(1, 1024, 4, 2, 128, 128, "bf16"))
+    assert L.stem_score_sam(ctypes.byref(d), None, ctypes.byref(kv), FAKE, FAKE, n, None) == sb.STEM_EINVAL
+    assert L.stem_score_sam(ctypes.byref(d), FAKE, ctypes.byref(kv), FAKE, FAKE, n - 1, None) == sb.STEM_EWORKSPACE
+    for args in ((None, FAKE, FAKE, FAKE), (FAKE, None, FAKE, FAKE), (FAKE, FAKE, None, FAKE),
+                 (FAKE, FAKE, FAKE, None)):
+        q, kbar, scores, ws = args
+        assert L.stem_score_pooled(ctypes.byref(d), q, kbar, FAKE, scores, ws, n, None) == sb.STEM_EINVAL
+    assert L.stem_score_pooled(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, n - 1, None) == sb.STEM_EWORKSPACE
+    for args in ((None, FAKE, FAKE, FAKE), (FAKE, None, FAKE, FAKE), (FAKE, FAKE, None, FAKE),
+                 (FAKE, FAKE, FAKE, None)):
+        k_in, v_in, kbar, lvn = args
+        assert L.stem_cache_write(ctypes.byref(d), k_in, v_in, ctypes.byref(kv), kbar, lvn, None) == sb.STEM_EINVAL
+    assert L.stem_cache_write(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, None) == sb.STEM_EINVAL
+    bad_page = sb.KvDesc(0x1000, 0x1000, 0x2000, 48, 32, 64)
+    assert L.stem_cache_write(ctypes.byref(d), FAKE, FAKE, ctypes.byref(bad_page), FAKE, FAKE, None) == sb.STEM_EINVAL
 
 
 def test_workspace_size_and_too_small_workspace():

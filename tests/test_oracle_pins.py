@@ -160,6 +160,105 @@ def test_zero_v_block_scores_minus_inf():
     assert np.all(np.isfinite(s[0, 0, 1:, 0]))
 
 
+def _sam_bruteforce(q, k, B, tau):
+    """Full token-level logits averaged over each B x B tile, with no value
+    information (the score-only metric of the Stem-en Deep Dive)."""
+    b, S, hq, d = q.shape
+    G = hq // k.shape[2]
+    nb = S // B
+    out = np.full((b, hq, nb, nb), -np.inf)
+    for bi in range(b):
+        for h in range(hq):
+            L = tau * q[bi, :, h] @ k[bi, :, h // G].T
+            for I in range(nb):
+                for J in range(I + 1):
+                    out[bi, h, I, J] = L[I * B:(I + 1) * B, J * B:(J + 1) * B].mean()
+    return out
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 2, 2, 8, 16), (2, 96, 4, 2, 16, 32), (1, 48, 3, 1, 4, 8)])
+def test_sam_equals_pairwise_block_mean(shape):
+    b, S, hq, hkv, d, B = shape
+    q, k, _ = _rand_qkv(13, b, S, hq, hkv, d)
+    got = oracle.sam_scores(q, k, B)
+    want = _sam_bruteforce(q, k, B, 1 / math.sqrt(d))
+    fin = np.isfinite(want)
+    assert np.array_equal(fin, np.isfinite(got))
+    assert np.max(np.abs(got[fin] - want[fin])) < 1e-12
+
+
+def test_sam_is_oam_with_equal_value_norms():
+    """Every V row of norm 5: the V term of every block is ln(sqrt(B) * 5), so
+    OAM exceeds SAM by exactly that constant on and below the diagonal."""
+    B, d = 8, 4
+    q, k, _ = _rand_qkv(15, 1, 64, 2, 1, d)
+    rng = np.random.default_rng(1)
+    v = np.zeros((1, 64, 1, d))
+    v[..., 0] = 3.0
+    v[..., 1] = 4.0 * np.sign(rng.standard_normal((1, 64, 1)))   # |row| = 5
+    oam = oracle.oam_scores(q, k, v, B)
+    sam = oracle.sam_scores(q, k, B)
+    low = np.tril(np.ones((8, 8), dtype=bool))
+    assert np.all(sam[..., ~low] == -np.inf)
+    assert np.allclose(oam[..., low] - sam[..., low], math.log(math.sqrt(B) * 5.0), atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# KV-cache write
+# --------------------------------------------------------------------------
+
+def test_quantize_e4m3_closed_forms():
+    # exact quotients: the rounding cases of E4M3 itself, after the division
+    cases = [(2.125, 2.0, 1.0), (2.375, 2.0, 1.25), (896.0, 2.0, 448.0), (1e30, 1.0, 448.0),
+             (-1e30, 1.0, -448.0), (3.0 * 2.0 ** -12, 0.25, 2.0 ** -8), (2.0 ** -11, 0.5, 0.0),
+             (0.0, 3.0, 0.0), (7.5, 0.5, 15.0)]
+    for x, scale, want in cases:
+        assert float(oracle.quantize_e4m3(x, scale)) == want, (x, scale)
+
+
+def test_quantize_e4m3_decides_on_the_single_precision_quotient():
+    """x / scale is formed in fp32, as torch's CPU float32 division forms it,
+    then cast by torch to float8_e4m3fn: both steps are library routines."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-12, 6, 20000))).astype(np.float32)
+    for scale in (0.0123, 1.0, 3.7, 2.0 ** -5):
+        xs = torch.from_numpy(x) / torch.tensor(scale, dtype=torch.float32)
+        keep = (xs.abs() <= 448.0).numpy()
+        want = xs[torch.from_numpy(keep)].to(torch.float8_e4m3fn).double().numpy()
+        got = oracle.quantize_e4m3(x[keep], scale)
+        assert np.array_equal(got, want), scale
+
+
+def test_cache_write_constant_rows():
+    """Constant rows: the stored value is the rounded quotient, kbar its
+    dequantised value, lvn = ln(sqrt(B * d) * |value|)."""
+    B, d, S = 16, 8, 64
+    k = np.full((1, S, 2, d), 0.7)
+    v = np.full((1, S, 2, d), -1.3)
+    ks, vs, kbar, lvn = oracle.cache_write(k, v, B, fp8=True, k_scale=0.01, v_scale=0.5)
+    # 0.7 / 0.01 is about 70, between the E4M3 values 64 and 72 (spacing 8 in
+    # [64, 128)): stored 72.  -1.3 / 0.5 = -2.6, between -2.5 and -2.75: -2.5.
+    assert np.all(ks == 72.0) and np.all(vs == -2.5)
+    assert np.allclose(kbar, 72.0 * 0.01, rtol=0, atol=1e-15)
+    assert np.allclose(lvn, math.log(math.sqrt(B * d) * 1.25), atol=1e-12)
+    ks2, vs2, kbar2, lvn2 = oracle.cache_write(k, v, B)
+    assert np.all(ks2 == 0.7) and np.allclose(kbar2, 0.7, rtol=0, atol=1e-15)
+    assert np.allclose(lvn2, math.log(math.sqrt(B * d) * 1.3), atol=1e-12)
+
+
+def test_cache_write_saturates_and_pools_per_block():
+    B, d = 4, 2
+    k = np.zeros((1, 8, 1, d))
+    k[0, :4] = 1000.0            # saturates at 448 (scale 1)
+    k[0, 4:] = [[[1.0, -2.0]], [[3.0, 0.5]], [[-1.0, 2.0]], [[1.0, 0.5]]]
+    v = np.ones((1, 8, 1, d))
+    ks, _, kbar, lvn = oracle.cache_write(k, v, B, fp8=True)
+    assert np.all(ks[0, :4] == 448.0)
+    assert np.array_equal(kbar[0, 0, 0], [448.0, 448.0])
+    assert np.array_equal(kbar[0, 0, 1], [1.0, 0.25])
+    assert np.allclose(lvn[0, 0], math.log(math.sqrt(B * d)), atol=1e-15)
+
+
 # --------------------------------------------------------------------------
 # TPD budget
 # --------------------------------------------------------------------------

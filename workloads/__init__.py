@@ -135,6 +135,41 @@ def make_inputs(w: Workload, device="cpu", gen_device: Optional[str] = None):
     return out
 
 
+def make_cache_inputs(w: Workload, device="cpu", gen_device: Optional[str] = None,
+                      fp8_scale: Optional[float] = None):
+    """Inputs of a KV-cache write for workload w: the new K and V ([b, S, Hkv,
+    d], drawn as make_inputs draws them) in the type the write reads (bf16 for
+    an FP8 or bf16 cache, fp32 for an fp32 cache); k_scale / v_scale (for an
+    FP8 cache amax / 448 of those values, or fp8_scale for both when given;
+    else 1.0); and, when paged, the block table of make_inputs and num_pages."""
+    gd = gen_device or "cpu"
+    b, S, hkv, d = w.batch, w.seq, w.hkv, w.head_dim
+    k = _randn((b, S, hkv, d), w.seed + 1, gd)
+    v = _randn((b, S, hkv, d), w.seed + 2, gd)
+    v.mul_(v_row_scale(w, gd)[:, :, None, None])
+    if w.sink:
+        k[:, :4].mul_(4.0)
+    out = {"k_scale": 1.0, "v_scale": 1.0}
+    if w.dtype == "f32":
+        out.update(k=k, v=v)
+    else:
+        out.update(k=k.to(torch.bfloat16), v=v.to(torch.bfloat16))
+        if w.dtype == "fp8":
+            for name in ("k", "v"):
+                amax = float(out[name].float().abs().max())
+                out[name + "_scale"] = fp8_scale if fp8_scale else (amax / FP8_MAX if amax > 0 else 1.0)
+    del k, v
+    for name in ("k", "v"):
+        out[name] = out[name].to(device).contiguous()
+    if w.paged:
+        pages_per_seq = S // w.page_size
+        num_pages = b * pages_per_seq
+        perm = torch.randperm(num_pages, generator=_gen(w.seed + 4, "cpu"))
+        out["block_table"] = perm.view(b, pages_per_seq).to(torch.int32).to(device)
+        out["num_pages"] = num_pages
+    return out
+
+
 def to_float64(x: torch.Tensor):
     """Exact upcast of a working-dtype tensor (fp8 codes included) to a float64
     numpy array.  Per-tensor scales are applied by the consumer."""
