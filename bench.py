@@ -155,6 +155,64 @@ def time_cache_write(w: wl.Workload, p, q, runs: int):
     }
 
 
+def time_decode(w: wl.Workload, p, k, v, table, page, ws_score, runs: int):
+    """One decode step over the full cache of the workload (the new token at
+    position seq_len - 1, keeping the TPD budget of the last row), with the
+    block representations stem_score left in its workspace.  Reports the step
+    time and the HBM bytes of the kept K/V blocks: summed over query heads
+    (what a per-head kernel requests) and as the union over each KV group's
+    heads (the least any kernel must read)."""
+    dev = "cuda"
+    nb = w.num_blocks
+    g = torch.Generator(device=dev).manual_seed(w.seed + 7)
+    q32 = torch.randn((w.batch, w.hq, w.head_dim), generator=g, device=dev)
+    pd = dataclasses.replace(p)
+    if w.dtype == "fp8":
+        q, qs = wl.quantize_fp8(q32)
+        pd.q_scale = float(qs)
+    else:
+        q = q32.to(torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    budget, _ = sb.stem_tpd_budget(nb, w.density, w.alpha)
+    lens = torch.full((w.batch,), w.seq, dtype=torch.int32, device=dev)
+    keep = torch.full((w.batch,), budget[nb - 1], dtype=torch.int32, device=dev)
+    al = lambda x: (x + 255) // 256 * 256
+    nq = w.batch * w.hq * nb * w.head_dim * 4
+    nk = w.batch * w.hkv * nb * w.head_dim * 4
+    kbar = ws_score[al(nq):al(nq) + nk].view(torch.float32).view(w.batch, w.hkv, nb, w.head_dim)
+    lvn = ws_score[al(nq) + al(nk):al(nq) + al(nk) + w.batch * w.hkv * nb * 4].view(torch.float32)
+    odt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    o = torch.empty((w.batch, w.hq, w.head_dim), dtype=odt, device=dev)
+    lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(sb.stem_decode_workspace_size(pd), dtype=torch.uint8, device=dev)
+    t = Timer()
+    sb.stem_decode(pd, q, k, v, lens, keep, kbar, lvn, o, lse, ws, table, page)
+    for _ in range(runs):
+        with t:
+            sb.stem_decode(pd, q, k, v, lens, keep, kbar, lvn, o, lse, ws, table, page)
+    torch.cuda.synchronize()
+    ms = sum(t.ms()) / runs
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    block_bytes = 2 * w.block * w.head_dim * es           # K and V of one block, one KV head
+    lists = ws[:w.batch * w.hq * nb * 4].view(torch.int32).view(w.batch, w.hq, nb)
+    kept = budget[nb - 1]
+    per_head = w.batch * w.hq * kept * block_bytes
+    group = w.hq // w.hkv
+    union = 0
+    for bi in range(w.batch):
+        for gg in range(w.hkv):
+            union += int(torch.unique(lists[bi, gg * group:(gg + 1) * group, :kept]).numel())
+    union *= block_bytes
+    return {
+        "decode_ms": ms,
+        "kept_blocks_per_head": kept,
+        "kv_bytes_per_head_sum": per_head,
+        "kv_bytes_group_union": union,
+        "gbs_per_head_sum": per_head / (ms * 1e-3) / 1e9,
+        "gbs_group_union": union / (ms * 1e-3) / 1e9,
+        "hbm_frac_per_head_sum": per_head / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
 class Timer:
     """HIP events on the stream the library launches on (torch's current stream)."""
 
@@ -235,6 +293,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip timing one decode step over the full cache")
     ap.add_argument("--no-cache-write", action="store_true",
                     help="skip timing the fused KV-cache write and scoring from its output")
     ap.add_argument("--source-hash", action="store_true",
@@ -367,6 +427,10 @@ def main():
         })
         log(f"[bench] dense {dense_ms:.3f} ms, density-1 sparse {full_ms:.3f} ms, "
             f"R {result['ratio_vs_dense']:.3f}")
+
+    if not args.no_decode:
+        log(f"[bench] decode step over the full cache, {args.dense_steps * 10} runs")
+        result["decode"] = time_decode(w, p, k, v, table, page, ws, args.dense_steps * 10)
 
     if not args.no_cache_write:
         log(f"[bench] fused KV-cache write and pooled scoring, {args.dense_steps} runs each")

@@ -24,7 +24,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Wall", "-Wno-unused-function"] + DEVICE_FLAGS
 
-SOURCES = ["api.cpp", "tpd.cpp", "score.hip", "select.hip", "bsa.hip"]
+SOURCES = ["api.cpp", "tpd.cpp", "score.hip", "select.hip", "bsa.hip", "decode.hip"]
 # The attention kernel never produces or consumes NaN (masked scores are -inf and
 # every -inf - -inf is guarded), so fmax needs no NaN quieting there.
 EXTRA = {"bsa.hip": ["-fno-honor-nans"]}

@@ -259,4 +259,34 @@ int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *k
     return hip_status(e, "bsa_prefill launch");
 }
 
+int stem_decode_workspace_size(const stem_attn_desc *desc, size_t *bytes) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if (!bytes) return fail(STEM_EINVAL, "bytes is NULL");
+    size_t a, b, c;
+    decode_workspace_layout(s, &a, &b, &c, bytes);
+    return ok();
+}
+
+int stem_decode(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                const int32_t *seq_lens, const int32_t *keep, const float *kbar, const float *lvn,
+                void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    Shape s;
+    KvView v;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if ((rc = check_kv(kv, s, &v))) return rc;
+    if (!q || !seq_lens || !o || !workspace) return fail(STEM_EINVAL, "q, seq_lens, o or workspace is NULL");
+    if (keep && !kbar) return fail(STEM_EINVAL, "kbar is NULL but keep is given");
+    size_t a, b, c, total;
+    decode_workspace_layout(s, &a, &b, &c, &total);
+    if (workspace_bytes < total)
+        return fail(STEM_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
+    if ((rc = hip_precheck())) return rc;
+    hipError_t e = launch_decode(s, q, v, seq_lens, keep, kbar, lvn, o, lse, workspace,
+                                 static_cast<hipStream_t>(stream));
+    return hip_status(e, "stem_decode launch");
+}
+
 }  // extern "C"

@@ -61,6 +61,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Order-preserving key of a score for top-k selection: larger score -> larger
+// key; NaN below everything (key 0); -0 == +0.
+__device__ __forceinline__ uint32_t order_key(float x) {
+    if (x != x) return 0u;
+    if (x == 0.0f) x = 0.0f;
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Number of set bits of `m` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));

@@ -27,14 +27,6 @@ struct SelectArgs {
     TpdPlan plan;
 };
 
-// Larger score -> larger key; NaN below everything (key 0); -0 == +0.
-__device__ __forceinline__ uint32_t order_key(float x) {
-    if (x != x) return 0u;
-    if (x == 0.0f) x = 0.0f;
-    const uint32_t u = __float_as_uint(x);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 template <int MAXC>
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     const int lane = threadIdx.x & 63;

@@ -89,5 +89,11 @@ hipError_t launch_select(const Shape &s, const TpdPlan &plan, const float *score
                          hipStream_t st);
 hipError_t launch_bsa(const Shape &s, const void *q, const KvView &kv, const uint32_t *mask,
                       void *o, float *lse, hipStream_t st);
+// Decode: workspace offsets (kept lists, counts, split partials) and launch.
+void decode_workspace_layout(const Shape &s, size_t *lists, size_t *counts, size_t *part,
+                             size_t *total);
+hipError_t launch_decode(const Shape &s, const void *q, const KvView &kv, const int32_t *seq_lens,
+                         const int32_t *keep, const float *kbar, const float *lvn, void *o,
+                         float *lse, void *workspace, hipStream_t st);
 
 }  // namespace stem

@@ -26,6 +26,8 @@
  *                      again (cn486.com article, §二.2.1: precomputed compact
  *                      block representations; §二.2.2: paged FP8 KV in vLLM).
  *   stem_score_pooled  scoring from those precomputed representations.
+ *   stem_decode        one decode step over the cache with Stem block
+ *                      selection for the new token.
  *
  * Conventions for every entry point
  *   - Tensors are row-major, in caller-owned DEVICE memory unless a comment
@@ -159,6 +161,44 @@ int stem_score_pooled(const stem_attn_desc *desc, const void *q, const float *kb
  * cache, so stem_score_pooled with them gives stem_score's scores. */
 int stem_cache_write(const stem_attn_desc *desc, const void *k_in, const void *v_in,
                      const stem_kv_desc *cache, float *kbar, float *lvn, void *stream);
+
+/* Bytes of scratch stem_decode needs.  After a call the workspace holds,
+ * each region starting on a 256-byte boundary, in this order:
+ *   lists  int32 [batch, num_q_heads, Nb]  kept blocks of each row, ascending
+ *   counts int32 [batch, num_q_heads]      number of kept blocks
+ * followed by the split-K partials. */
+int stem_decode_workspace_size(const stem_attn_desc *desc, size_t *bytes);
+
+/* One decode step of Stem block-sparse attention: for every sequence b and
+ * query head h, the new token (position t = seq_lens[b] - 1, block
+ * I = t / block_size) scores the complete blocks J in [1, I-1] of its cache
+ * with the OAM metric (Stem article on cn486.com, §一.3.2, the token standing
+ * for its query block), keeps J = 0, J = I and the best keep[b] - |{0, I}|
+ * of them (score descending, equal scores to the smaller J), and attends to
+ * the keys j <= t of the kept blocks only (the memory-bound decode case of
+ * the BLASST summary, §2.3: skipped blocks are never read).
+ *   desc:     shape of the cache: seq_len is its capacity per sequence (a
+ *             multiple of block_size); dtype, scales and softmax scale as for
+ *             bsa_prefill.
+ *   q:        [batch, num_q_heads, head_dim] in desc->dtype (FP8 codes with
+ *             q_scale).
+ *   kv:       the cache (contiguous or paged), holding tokens 0..t of every
+ *             sequence, the new token's K and V included.
+ *   seq_lens: device int32 [batch], tokens in each sequence including the new
+ *             one; values outside [1, seq_len] are clamped into it.
+ *   keep:     device int32 [batch], blocks to keep for the new token's row
+ *             (for the prefill's TPD budget: stem_tpd_budget over I + 1 rows,
+ *             entry I), clamped to [|{0, I}|, I + 1]; NULL keeps every block
+ *             (dense decode).
+ *   kbar, lvn: the cache's block representations as stem_cache_write
+ *             produces them (only complete blocks J < I are read); lvn NULL
+ *             scores without the value term; both unused when keep is NULL.
+ *   o:        [batch, num_q_heads, head_dim], bf16 (fp32 for STEM_F32).
+ *   lse:      optional fp32 [batch, num_q_heads], natural log.
+ *   workspace: at least stem_decode_workspace_size() bytes. */
+int stem_decode(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                const int32_t *seq_lens, const int32_t *keep, const float *kbar, const float *lvn,
+                void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /* TPD budget on the host (Stem article §一.3.1; setupai.cc "Technical Deep
  * Dive").  T = floor(density * Nb(Nb+1)/2 + 1/2) computed in double, clamped

@@ -26,6 +26,7 @@ from .stem import (  # noqa: F401
     block_sparse_attention,
     cache_write,
     causal_block_count,
+    decode_step,
     dense_causal_attention,
     dequantize,
     e4m3fn_round,

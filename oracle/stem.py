@@ -392,6 +392,62 @@ def attention_rows(q, k, v, block_mask, block, rows, softmax_scale=None):
     return out_o, out_l
 
 
+def decode_step(q, k, v, seq_lens, block, keep=None, softmax_scale=None, value_term=True):
+    """One decode step with Stem block selection for the new token.
+
+    q [b, Hq, d]: the new token of each sequence; k, v [b, S, Hkv, d]: the
+    cache (dequantised), sequence b holding tokens 0 .. seq_lens[b]-1 with the
+    new token last, at t = seq_lens[b] - 1 in block I = t // block.
+    The token scores the complete blocks J in [1, I-1] as OAM does a query
+    block (Stem-cn §一.3.2, the token standing for its block's mean), with the
+    block representations of pool_blocks; keep[b] blocks are kept by the rule
+    of select_row (sink and own block forced), keep clamped to
+    [|{0, I}|, I + 1]; keep None keeps every block.  Attention then sees the
+    keys j <= t of the kept blocks (as in _attend).
+    Returns (o [b, Hq, d], lse [b, Hq], kept) with kept[b][h] the sorted
+    kept blocks."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b, Hq, d = q.shape
+    Hkv = k.shape[2]
+    group = Hq // Hkv
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = np.zeros((b, Hq, d))
+    lse = np.zeros((b, Hq))
+    kept = []
+    for bi in range(b):
+        t = int(seq_lens[bi]) - 1
+        I = t // block
+        if I > 0 and keep is not None:
+            done = slice(bi, bi + 1), slice(0, I * block)
+            _, kbar, lvn = pool_blocks(k[done], k[done], v[done], block)
+        kept_b = []
+        for h in range(Hq):
+            g = h // group
+            if keep is None:
+                row_kept = list(range(I + 1))
+            else:
+                forced = 1 if I == 0 else 2
+                budget = min(max(int(keep[bi]), forced), I + 1)
+                row = np.full(I + 1, -np.inf)
+                if I > 1:
+                    row[1:I] = tau * (kbar[0, g, 1:I] @ q[bi, h])
+                    if value_term:
+                        row[1:I] += lvn[0, g, 1:I]
+                row_kept = select_row(row, I, budget)
+            kept_b.append(row_kept)
+            mrow = np.zeros(I + 1, dtype=bool)
+            mrow[row_kept] = True
+            keys_idx, diag = _visible_keys(mrow, I, block)
+            oo, ll = _attend(q[bi, h][None, :], np.array([t]), keys_idx, diag, I, block,
+                             k[bi, :, g], v[bi, :, g], tau)
+            o[bi, h] = oo[0]
+            lse[bi, h] = ll[0]
+        kept.append(kept_b)
+    return o, lse, kept
+
+
 def dense_causal_attention(q, k, v, softmax_scale=None):
     """Plain causal softmax attention, row by row over all keys j <= i: the
     dense baseline (Stem-cn §二.3) and the density-1 limit of the sparse path."""

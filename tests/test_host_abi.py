@@ -111,6 +111,28 @@ def test_new_entry_points_reject_nulls_and_small_workspace():
     assert L.stem_cache_write(ctypes.byref(d), FAKE, FAKE, ctypes.byref(bad_page), FAKE, FAKE, None) == sb.STEM_EINVAL
 
 
+def test_decode_rejects_nulls_and_small_workspace():
+    d = _desc()
+    L = sb.lib()
+    kv = sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
+    n = sb.stem_decode_workspace_size(sb.Problem(1, 1024, 4, 2, 128, 128, "bf16"))
+    ok = dict(q=FAKE, seq=FAKE, keep=FAKE, kbar=FAKE, lvn=FAKE, o=FAKE, ws=FAKE)
+
+    def rc(**kw):
+        a = dict(ok, **kw)
+        return L.stem_decode(ctypes.byref(d), a["q"], ctypes.byref(kv), a["seq"], a["keep"], a["kbar"],
+                             a["lvn"], a["o"], None, a["ws"], kw.get("n", n), None)
+    for name in ("q", "seq", "o", "ws"):
+        assert rc(**{name: None}) == sb.STEM_EINVAL, name
+    assert rc(kbar=None) == sb.STEM_EINVAL                     # keep given without kbar
+    assert rc(n=n - 1) == sb.STEM_EWORKSPACE
+    assert L.stem_decode(ctypes.byref(d), FAKE, None, FAKE, None, None, None, FAKE, None, FAKE, n,
+                         None) == sb.STEM_EINVAL
+    bad = _desc(head_dim=96)
+    assert L.stem_decode(ctypes.byref(bad), FAKE, ctypes.byref(kv), FAKE, None, None, None, FAKE, None,
+                         FAKE, n, None) == sb.STEM_EUNSUPPORTED
+
+
 def test_workspace_size_and_too_small_workspace():
     p = sb.Problem(2, 1024, 4, 2, 128, 128, "bf16")
     n = sb.stem_score_workspace_size(p)

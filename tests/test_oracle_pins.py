@@ -527,6 +527,62 @@ def test_attention_rows_matches_full():
 
 
 # --------------------------------------------------------------------------
+# Decode
+# --------------------------------------------------------------------------
+
+def test_dense_decode_equals_sdpa_and_ignores_tokens_past_the_end():
+    rng = np.random.default_rng(21)
+    b, S, hq, hkv, d, B = 2, 96, 4, 2, 16, 16
+    q = rng.standard_normal((b, hq, d))
+    k = rng.standard_normal((b, S, hkv, d))
+    v = rng.standard_normal((b, S, hkv, d))
+    lens = [37, 96]
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 37:] = 1e6                               # past the end of sequence 0
+    v2[0, 37:] = -1e6
+    o, lse, kept = oracle.decode_step(q, k2, v2, lens, B)
+    tau = 1 / math.sqrt(d)
+    for bi in range(b):
+        n = lens[bi]
+        assert kept[bi][0] == list(range((n - 1) // B + 1))
+        for h in range(hq):
+            g = h // (hq // hkv)
+            qt = torch.from_numpy(q[bi, h]).view(1, 1, 1, d)
+            kt = torch.from_numpy(k[bi, :n, g]).view(1, 1, n, d)
+            vt = torch.from_numpy(v[bi, :n, g]).view(1, 1, n, d)
+            want = F.scaled_dot_product_attention(qt, kt, vt, scale=tau).view(d).numpy()
+            assert np.max(np.abs(o[bi, h] - want)) < 1e-12
+            want_lse = torch.logsumexp(tau * (kt.view(n, d) @ qt.view(d)), 0).item()
+            assert abs(lse[bi, h] - want_lse) < 1e-12
+
+
+@pytest.mark.parametrize("t,keep", [(16 * 5 + 3, 3), (16 * 6 - 1, 4), (16 * 7, 2), (16 * 6 + 8, 7), (5, 3)])
+def test_decode_equals_prefill_row_of_a_constant_query_block(t, keep):
+    """A query block made of B copies of the new token has the token as its
+    mean, so the prefill path (OAM scores, select_row, block-sparse attention)
+    must keep the same blocks for that row and give the same output at t."""
+    rng = np.random.default_rng(t)
+    b, hq, hkv, d, B = 1, 4, 2, 8, 16
+    I = t // B
+    S = (I + 1) * B
+    k = rng.standard_normal((b, S, hkv, d))
+    v = rng.standard_normal((b, S, hkv, d)) * np.exp(rng.standard_normal((b, S, 1, 1)))
+    q_full = rng.standard_normal((b, S, hq, d))
+    qt = rng.standard_normal((b, hq, d))
+    q_full[0, I * B:(I + 1) * B] = qt[0]
+    o, lse, kept = oracle.decode_step(qt, k, v, [t + 1], B, keep=[keep])
+    s = oracle.oam_scores(q_full, k, v, B)
+    budget = [1] + [2] * I
+    budget[I] = min(max(keep, 1 if I == 0 else 2), I + 1)
+    mask = oracle.select_blocks(s, budget)
+    o_p, lse_p = oracle.block_sparse_attention(q_full, k, v, mask, B)
+    for h in range(hq):
+        assert kept[0][h] == list(np.nonzero(mask[0, h, I])[0])
+        assert np.max(np.abs(o[0, h] - o_p[0, t, h])) < 1e-12
+        assert abs(lse[0, h] - lse_p[0, h, t]) < 1e-12
+
+
+# --------------------------------------------------------------------------
 # FP8 E4M3 rounding
 # --------------------------------------------------------------------------
 
