@@ -1203,6 +1203,373 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
 }
 
+// ---------------------------------------------------------------------------
+// BF16, d = 128, 128-token blocks: the pipeline of bsa_fp8_kernel with bf16
+// operands (v_mfma_f32_32x32x16_bf16: per block and wave 16 MFMAs of
+// S = K(j+1) Q^T and 16 of O += V(j-1)^T P(j-1), interleaved with the softmax
+// of block j).  A K or V block is 32 KB in LDS, so there are two stages of
+// each and the loads run one block ahead: K(j+2) and V(j) are loaded during
+// block j and waited for at the next block's barrier.  P is rounded to bf16
+// with no scale, and O is normalised by the exact fp32 sum of P.
+//
+// LDS swizzles of the 16-byte chunks of a 256-byte row.  K: chunk c of row r
+// sits at c ^ (r & 15), so the 16 rows a 16-lane group reads for one MFMA
+// step land on 16 distinct chunk positions, and a lane's address for step s
+// is its base XOR 32 s.  V: chunk c of row r sits at c ^ ((r & 3) << 2), so
+// the 4 rows x 2 chunks of one transposing read land on 8 distinct positions,
+// and every V operand address is one of four per-lane registers (one per d
+// tile) plus an immediate.
+namespace bf16p {
+constexpr int D = 128, BLK = 128, NT = 512, NW = 8;
+constexpr int ROWB = D * 2;                      // bytes of a K or V row
+constexpr int TILE = BLK * ROWB;                 // bytes of a K or V block
+constexpr int KST = 0, VST = 2 * TILE;           // two K stages, then two V stages
+constexpr int LIST_OFF = 4 * TILE;               // kept-block list (u16) after the stages
+constexpr int LIST = 4096;
+constexpr int WSUM_OFF = LIST_OFF + 2 * LIST;    // per-wave counts of the list scan
+constexpr int ML_OFF = WSUM_OFF + 4 * NW;        // (M, l) of the second key half
+constexpr int SMEM = ML_OFF + 2 * 4 * 64 * 4;
+constexpr float THRESH = 8.0f;                   // lazy rescale: P stays below 2^THRESH
+constexpr float M_NONE = -3.0e38f;               // running max before any finite score
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
+}  // namespace bf16p
+
+template <bool SPARSE, bool PAGED>
+__global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
+    using namespace bf16p;
+    using fp8p::buffer_rsrc;
+    using fp8p::const_i32;
+    using fp8p::i32x4;
+    using fp8p::load_lds16;
+    using fp8p::sync_vm;
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+    uint16_t *list = reinterpret_cast<uint16_t *>(smem + LIST_OFF);
+    int *wave_sum = reinterpret_cast<int *>(smem + WSUM_OFF);
+    float *part_ml = reinterpret_cast<float *>(smem + ML_OFF);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g32 = lane >> 5, r32 = lane & 31;
+    const int wq = wave & 3;                               // query group: rows 32 wq .. 32 wq + 31
+    const int ks = wave >> 2;                              // key half: keys 64 ks .. 64 ks + 63 of each block
+
+    // heaviest query blocks first; the heads of one KV group on one XCD
+    const int wg = blockIdx.x;
+    const int qidx = wg / a.hq, jh = wg % a.hq;
+    const int I = a.nb - 1 - qidx / a.batch;
+    const int b = qidx % a.batch;
+    const int h = (a.hq % 8 == 0) ? (jh % 8) * (a.hq / 8) + jh / 8 : jh;
+    const int g = h / (a.hq / a.hkv);
+
+    const int qrow = 32 * wq + r32;
+    const int token = I * BLK + qrow;
+    QFrag<kBF16, D> qf;                                    // in flight while the list is built
+    load_q<kBF16, D>(qf, a.q + (((size_t)b * a.seq + token) * a.hq + h) * (size_t)ROWB, g32);
+    const int n = build_block_list<NW, SPARSE>(a, b, h, I, list, wave_sum, tid, lane, wave);
+    if (n == 0) {
+        if (ks == 0) write_empty_row<kBF16, D>(a, b, h, token, g32);
+        return;
+    }
+    // Q has landed before the first load into LDS (those loads are not counted
+    // by the compiler, so a later wait for Q would drain them too).
+    asm volatile("" :: "v"(qf.u[0]), "v"(qf.u[1]), "v"(qf.u[2]), "v"(qf.u[3]));
+    asm volatile("" :: "v"(qf.u[4]), "v"(qf.u[5]), "v"(qf.u[6]), "v"(qf.u[7]));
+
+    // K operand of S = K Q^T: row kkey (+32 for the second tile), d chunk
+    // 2 s + g32 at position (2 s + g32) ^ (kkey & 15): base XOR 32 s.
+    const int kkey = 64 * ks + keymap<kBF16>(0, r32);
+    const int kbase = kkey * ROWB + 16 * (g32 ^ swz_k(kkey));
+    // V^T operand of d tile dt: rows vrow + (32 t + 16 hh + 4 q) of a V stage,
+    // chunk 4 dt + 2 ((lane >> 4) & 1) + ((lane & 3) >> 1), byte half lane & 1.
+    const int i16 = lane & 15;
+    const int vrow = 64 * ks + 8 * g32 + (i16 >> 2);
+    int vbase[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+        vbase[dt] = VST + vrow * ROWB + (((4 * dt + 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1)) ^ swz_v(vrow)) << 4) +
+                    8 * (i16 & 1);
+
+    // Global -> LDS: wave w moves rows 16 w + 4 i + (lane >> 4) of a block
+    // (i = 0..3) into LDS chunk position lane & 15 of the row; its 16 rows lie
+    // in one page.
+    const unsigned row_bytes = (unsigned)a.hkv * ROWB;
+    int dk[4], dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * i + (lane >> 4), cl = lane & 15;
+        dk[i] = (4 * i + (lane >> 4)) * (int)row_bytes + ((cl ^ swz_k(row)) << 4);
+        dv[i] = (4 * i + (lane >> 4)) * (int)row_bytes + ((cl ^ swz_v(row)) << 4);
+    }
+    auto list_at = [&](int i) { return SPARSE ? __builtin_amdgcn_readfirstlane((int)list[i]) : i; };
+    const int last = n - 1;
+    if constexpr (SPARSE) {
+        // pad the list with copies of its last entry, so that reads ahead need no clamp
+        if (tid < 8) list[n + tid] = list[last];
+    }
+    const_i32 *table = PAGED ? (const_i32 *)a.table + b * a.pages_per_seq : nullptr;
+    auto page_of = [&](int tok) -> int { return PAGED ? table[(unsigned)tok >> a.page_log2] : 0; };
+    auto row_off = [&](int tok, int page) -> unsigned {
+        unsigned row;
+        if constexpr (PAGED) row = ((unsigned)page << a.page_log2) | (unsigned)(tok & ((1 << a.page_log2) - 1));
+        else row = (unsigned)(b * a.seq + tok);
+        return row * row_bytes + (unsigned)g * ROWB;
+    };
+    auto tok_of = [&](int J) { return J * BLK + 16 * wave; };
+    auto src_off = [&](int J) -> unsigned { return row_off(tok_of(J), page_of(tok_of(J))); };
+    auto list_raw = [&](int i) -> int { return SPARSE ? (int)list[i] : min(i, last); };   // i <= n + 7
+    const i32x4 krs = buffer_rsrc(a.k), vrs = buffer_rsrc(a.v);
+    const unsigned lds_wave = (unsigned)(size_t)(lds_char *)smem + 16 * wave * ROWB;
+    auto dma = [&](i32x4 rs, auto STAGE_OFF, unsigned so, const int (&vo)[4]) {
+        constexpr int OFF = decltype(STAGE_OFF)::value;
+        load_lds16<OFF>(rs, lds_wave, (unsigned)vo[0], so);
+        load_lds16<OFF + 4 * ROWB>(rs, lds_wave, (unsigned)vo[1], so);
+        load_lds16<OFF + 8 * ROWB>(rs, lds_wave, (unsigned)vo[2], so);
+        load_lds16<OFF + 12 * ROWB>(rs, lds_wave, (unsigned)vo[3], so);
+    };
+    using std::integral_constant;
+
+    auto qop = [&](int st) { return __builtin_bit_cast(bf16x8, qf.u[st]); };
+    // K operand of tile t, d step st, from the K stage at byte offset ko
+    auto kop = [&](int ko, int t, int st) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(smem + ko + (kbase ^ (32 * st)) + t * 32 * ROWB));
+    };
+    // V^T operand of d tile dt, keys 32 t + 16 hh of this wave's half, V stage vo (from VST)
+    auto vop = [&](int vo, int t, int hh, int dt) {
+        const char *p = smem + vo + vbase[dt] + (32 * t + 16 * hh) * ROWB;
+        const i16x4 v0 = lds_tr16(p), v1 = lds_tr16(p + 4 * ROWB);
+        return __builtin_bit_cast(bf16x8, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+    };
+    auto mfma16 = [](const bf16x8 &x, const bf16x8 &y, const f32x16 &acc) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, acc, 0, 0, 0);
+    };
+
+    const float c = a.c_exp2;
+    const float ninf = -__builtin_huge_valf();
+    f32x16 o[4] = {};
+    float M = M_NONE, Mthr = M_NONE;                       // running max (log2 units) and M + THRESH
+    float l = 0.0f;                                        // this lane's exact sum of P (relative to 2^M)
+    f32x16 s[2] = {};                                      // scores of the block awaiting softmax
+    bf16x8 pk[4] = {};                                     // P of the block awaiting PV (zero before the first)
+    const int jdiag = list_at(last) == I ? last : -1;      // the diagonal block, if kept, is the last
+
+    // ---- prologue: K(0), K(1) and, standing in for V(-1) (multiplied by P = 0,
+    // so it only has to be finite), a copy of V(0) in V stage 1
+    {
+        const unsigned s0 = src_off(list_at(0));
+        dma(krs, integral_constant<int, KST>{}, s0, dk);
+        dma(krs, integral_constant<int, KST + TILE>{}, src_off(list_at(min(1, last))), dk);
+        dma(vrs, integral_constant<int, VST + TILE>{}, s0, dv);
+    }
+    // Row lookups run ahead of the loads that use them: the list entry is read
+    // at the end of iteration i-3, the page-table entry at the end of i-2, the
+    // offset formed at the end of i-1, for the loads of iteration i (K(i+2), V(i)).
+    unsigned so_k = src_off(list_at(min(2, last))), so_v = src_off(list_at(0));        // iteration 0
+    int tk = tok_of(list_at(min(3, last))), tv = tok_of(list_at(min(1, last)));       // iteration 1
+    int pgk = page_of(tk), pgv = page_of(tv);
+    int lk = list_raw(min(4, last)), lv = list_raw(min(2, last));                     // iteration 2
+    sync_vm<0, true>();                                    // K(0), K(1) have landed
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) s[t] = mfma16(kop(KST, t, st), qop(st), s[t]);
+
+    float alpha = 1.0f;                                    // rescale of O still to apply
+    auto rescale_o = [&]() {
+        if (__ballot(alpha != 1.0f)) {
+            asm volatile("");                              // (a real branch: taken a few times per row)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        }
+    };
+    f32x16 sB[2];
+    bf16x8 pkB[4] = {};
+    auto iter = [&](auto RR, int j) {
+        constexpr int R = decltype(RR)::value;              // j & 1
+        constexpr int KRD = KST + (1 - R) * TILE;           // K(j+1)
+        constexpr int VRD = (1 - R) * TILE;                 // V(j-1), from VST
+        constexpr int KDM = KST + R * TILE, VDM = VST + R * TILE;   // stages being loaded
+        f32x16(&sc)[2] = R ? sB : s;                        // scores of block j
+        f32x16(&sn)[2] = R ? s : sB;                        // scores of block j+1
+        bf16x8(&pv_in)[4] = R ? pkB : pk;                   // P(j-1)
+        bf16x8(&pv_out)[4] = R ? pk : pkB;                  // P(j)
+
+        // K(j+1) and V(j-1) have landed; K stage R and V stage R are free
+        sync_vm<0, true>();
+        rescale_o();
+        if (j == jdiag) {                                  // causal mask inside the diagonal block
+            asm volatile("");                              // (a real branch: taken once per row)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (keymap<kBF16>(2 * ks + t, 8 * (e >> 2) + 4 * g32 + (e & 3)) > qrow) sc[t][e] = ninf;
+        }
+#define SB() __builtin_amdgcn_sched_barrier(0)
+        auto dma_k = [&](auto I) {
+            load_lds16<KDM + 4 * decltype(I)::value * ROWB>(krs, lds_wave, (unsigned)dk[I], so_k);
+        };
+        auto dma_v = [&](auto I) {
+            load_lds16<VDM + 4 * decltype(I)::value * ROWB>(vrs, lds_wave, (unsigned)dv[I], so_v);
+        };
+        auto max3 = [](float x, float y, float z) { return fmaxf(x, fmaxf(y, z)); };
+        auto tile_max = [&](const f32x16 &x, float &u, float &v) {
+            u = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8]));
+            v = max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]);
+        };
+        float ls[4];
+        auto expq = [&](int t, int e0) {                   // P of 4 scores, into the partial sums
+#pragma unroll
+            for (int e = e0; e < e0 + 4; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(sc[t][e], c, -M));
+                sc[t][e] = pe;
+                ls[e & 3] = (t == 0 && e0 == 0) ? pe : ls[e & 3] + pe;
+            }
+        };
+        auto packq = [&](int w) {                          // 8 P of word w as bf16
+            const f32x16 &src = sc[w >> 1];
+            const int e0 = 8 * (w & 1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv_out[w][e] = (__bf16)src[e0 + e];
+        };
+        // ---- the region: 32 MFMA slots.  Slots 0-15: S(j+1) tile (k & 1), d
+        // step k / 2; slots 16-31: O tile (k & 3) += keys (k - 16) / 4 of V(j-1).
+        // Each LDS operand is read one slot ahead; the loads into LDS go out in
+        // the first eight slots; the softmax of block j is spread over the rest.
+        bf16x8 opk = kop(KRD, 0, 0);
+        float m0, m1, m2, m3, mx = 0.0f;
+        auto slot = [&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            // operand of the next slot
+            bf16x8 nxt;
+            if constexpr (k + 1 < 16) nxt = kop(KRD, (k + 1) & 1, (k + 1) >> 1);
+            else if constexpr (k + 1 < 32) nxt = vop(VRD, (k + 1 - 16) >> 3, ((k + 1 - 16) >> 2) & 1, (k + 1) & 3);
+            SB();
+            if constexpr (k < 16) sn[k & 1] = mfma16(opk, qop(k >> 1), k < 2 ? f32x16{} : sn[k & 1]);
+            else o[k & 3] = mfma16(opk, pv_in[((k - 16) >> 2)], o[k & 3]);
+            SB();
+            if constexpr (k < 4) dma_k(integral_constant<int, k>{});
+            else if constexpr (k < 8) dma_v(integral_constant<int, k - 4>{});
+            // softmax work of this slot
+            if constexpr (k == 0) tile_max(sc[0], m0, m1);
+            if constexpr (k == 1) tile_max(sc[1], m2, m3);
+            if constexpr (k == 2) {
+                mx = max_xor32(fmaxf(max3(m0, m1, m2), m3));
+                const float xm = mx * c;                       // the block's row max in log2 units
+                const float Mn = xm > Mthr ? xm : M;           // lazy: move only past M + THRESH
+                alpha = __builtin_amdgcn_exp2f(M - Mn);        // 1 unless the max moved
+                M = Mn;
+                Mthr = Mn + THRESH;
+            }
+            if constexpr (k >= 3 && k < 27 && (k - 3) % 3 == 0) expq(((k - 3) / 3) >> 2, 4 * (((k - 3) / 3) & 3));
+            if constexpr (k >= 5 && k < 29 && (k - 5) % 3 == 0 && ((k - 5) / 3) & 1) packq(((k - 5) / 3) >> 1);
+            if constexpr (k + 1 < 32) opk = nxt;
+        };
+        slot(integral_constant<int, 0>{});
+        slot(integral_constant<int, 1>{});
+        slot(integral_constant<int, 2>{});
+        slot(integral_constant<int, 3>{});
+        slot(integral_constant<int, 4>{});
+        slot(integral_constant<int, 5>{});
+        slot(integral_constant<int, 6>{});
+        slot(integral_constant<int, 7>{});
+        slot(integral_constant<int, 8>{});
+        slot(integral_constant<int, 9>{});
+        slot(integral_constant<int, 10>{});
+        slot(integral_constant<int, 11>{});
+        slot(integral_constant<int, 12>{});
+        slot(integral_constant<int, 13>{});
+        slot(integral_constant<int, 14>{});
+        slot(integral_constant<int, 15>{});
+        slot(integral_constant<int, 16>{});
+        slot(integral_constant<int, 17>{});
+        slot(integral_constant<int, 18>{});
+        slot(integral_constant<int, 19>{});
+        slot(integral_constant<int, 20>{});
+        slot(integral_constant<int, 21>{});
+        slot(integral_constant<int, 22>{});
+        slot(integral_constant<int, 23>{});
+        slot(integral_constant<int, 24>{});
+        slot(integral_constant<int, 25>{});
+        slot(integral_constant<int, 26>{});
+        slot(integral_constant<int, 27>{});
+        slot(integral_constant<int, 28>{});
+        slot(integral_constant<int, 29>{});
+        slot(integral_constant<int, 30>{});
+        slot(integral_constant<int, 31>{});
+        l = fmaf(l, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+        SB();
+#undef SB
+        // ---- lookups, after the region: they complete across the barrier
+        so_k = row_off(tk, pgk);                           // iteration j+1
+        so_v = row_off(tv, pgv);
+        tk = tok_of(__builtin_amdgcn_readfirstlane(lk));   // iteration j+2
+        tv = tok_of(__builtin_amdgcn_readfirstlane(lv));
+        pgk = page_of(tk);
+        pgv = page_of(tv);
+        lk = list_raw(j + 5);                              // iteration j+3
+        lv = list_raw(j + 3);
+    };
+    for (int j = 0; j < n; j += 2) {
+        iter(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < n) iter(std::integral_constant<int, 1>{}, j + 1);
+    }
+    sync_vm<0>();                                          // V(n-1) has landed
+    rescale_o();
+    {
+        // block n-1 ran as an iteration with R = (n-1) & 1: its P is in pk for odd R
+        const bool odd = ((n - 1) & 1) != 0;
+        const int vo = ((n - 1) & 1) * TILE;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const bf16x8 pl = odd ? pk[w] : pkB[w];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma16(vop(vo, w >> 1, w & 1, dt), pl, o[dt]);
+        }
+    }
+
+    // ---- merge the key halves, normalise, store -------------------------------
+    l = sum_xor32(l);
+    sync_vm<0, true>();                                    // every load into LDS is done: stages are free
+    float *po = reinterpret_cast<float *>(smem) + wq * 64 * (D / 2);
+    if (ks == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) po[(dt * 16 + e) * 64 + lane] = o[dt][e];
+        part_ml[(2 * wq) * 64 + lane] = M;
+        part_ml[(2 * wq + 1) * 64 + lane] = l;
+    }
+    __syncthreads();
+    if (ks == 1) return;
+    const float M1 = part_ml[(2 * wq) * 64 + lane];
+    const float l1 = part_ml[(2 * wq + 1) * 64 + lane];
+    const float mm = fmaxf(M, M1);
+    const float a0 = __builtin_amdgcn_exp2f(M - mm), a1 = __builtin_amdgcn_exp2f(M1 - mm);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] = o[dt][e] * a0 + po[(dt * 16 + e) * 64 + lane] * a1;
+    l = l * a0 + l1 * a1;
+    const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
+    const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * dt + 8 * i + 4 * g32;
+            u32x2 u;
+            u.x = f32_to_bf16_bits(o[dt][4 * i] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 1] * inv) << 16);
+            u.y = f32_to_bf16_bits(o[dt][4 * i + 2] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 3] * inv) << 16);
+            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = u;
+        }
+    if (a.lse && g32 == 0)
+        a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
+}
+
 template <int DT, int D, int BLK>
 hipError_t launch_cfg(const BsaArgs &a, bool sparse, hipStream_t st) {
     using G = Geo<DT, D, BLK>;
@@ -1213,6 +1580,11 @@ hipError_t launch_cfg(const BsaArgs &a, bool sparse, hipStream_t st) {
         else if (sparse) hipLaunchKernelGGL((bsa_fp8_kernel<true, false>), grid, dim3(fp8p::NT), 0, st, a);
         else if (paged) hipLaunchKernelGGL((bsa_fp8_kernel<false, true>), grid, dim3(fp8p::NT), 0, st, a);
         else hipLaunchKernelGGL((bsa_fp8_kernel<false, false>), grid, dim3(fp8p::NT), 0, st, a);
+    } else if constexpr (DT == kBF16 && D == 128 && BLK == 128) {
+        if (sparse && paged) hipLaunchKernelGGL((bsa_bf16_kernel<true, true>), grid, dim3(bf16p::NT), 0, st, a);
+        else if (sparse) hipLaunchKernelGGL((bsa_bf16_kernel<true, false>), grid, dim3(bf16p::NT), 0, st, a);
+        else if (paged) hipLaunchKernelGGL((bsa_bf16_kernel<false, true>), grid, dim3(bf16p::NT), 0, st, a);
+        else hipLaunchKernelGGL((bsa_bf16_kernel<false, false>), grid, dim3(bf16p::NT), 0, st, a);
     } else {
         if (sparse && paged) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, true, true>), grid, dim3(G::NT), 0, st, a);
         else if (sparse) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, true, false>), grid, dim3(G::NT), 0, st, a);

@@ -54,6 +54,9 @@ SMALL = [
     wl.Workload("bf16-single-block", 1, 128, 2, 1, 128, 128, "bf16"),
     wl.Workload("bf16-alpha0-dense-ish", 1, 128 * 24, 2, 1, 128, 128, "bf16", density=0.7, alpha=0.0),
     wl.Workload("bf16-alpha1", 1, 128 * 24, 2, 1, 128, 128, "bf16", density=0.3, alpha=1.0),
+    wl.Workload("bf16-paged16-d128-b128", 2, 128 * 19, 4, 2, 128, 128, "bf16", paged=True, page_size=16),
+    wl.Workload("bf16-paged128-d128-b128", 1, 128 * 23, 8, 1, 128, 128, "bf16", paged=True, page_size=128,
+                density=0.5),
 ]
 
 
