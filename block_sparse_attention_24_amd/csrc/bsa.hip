@@ -1439,17 +1439,23 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
         // step k / 2; slots 16-31: O tile (k & 3) += keys (k - 16) / 4 of V(j-1).
         // Each LDS operand is read one slot ahead; the loads into LDS go out in
         // the first eight slots; the softmax of block j is spread over the rest.
-        bf16x8 opk = kop(KRD, 0, 0);
+        // MFMA m < 16: S(j+1) tile m & 1, d step m / 2; m >= 16: O tile m & 3
+        // += keys 16 ((m - 16) / 4) of V(j-1).  Slot k issues MFMA order(k).
+        auto order = [](int k) { return k; };
+        auto operand = [&](int m) {
+            if (m < 16) return kop(KRD, m & 1, m >> 1);
+            return vop(VRD, (m - 16) >> 3, ((m - 16) >> 2) & 1, m & 3);
+        };
+        bf16x8 opk = operand(order(0));
         float m0, m1, m2, m3, mx = 0.0f;
         auto slot = [&](auto KK) {
             constexpr int k = decltype(KK)::value;
-            // operand of the next slot
+            constexpr int m = order(k);
             bf16x8 nxt;
-            if constexpr (k + 1 < 16) nxt = kop(KRD, (k + 1) & 1, (k + 1) >> 1);
-            else if constexpr (k + 1 < 32) nxt = vop(VRD, (k + 1 - 16) >> 3, ((k + 1 - 16) >> 2) & 1, (k + 1) & 3);
+            if constexpr (k + 1 < 32) nxt = operand(order(k + 1));   // operand of the next slot
             SB();
-            if constexpr (k < 16) sn[k & 1] = mfma16(opk, qop(k >> 1), k < 2 ? f32x16{} : sn[k & 1]);
-            else o[k & 3] = mfma16(opk, pv_in[((k - 16) >> 2)], o[k & 3]);
+            if constexpr (m < 16) sn[m & 1] = mfma16(opk, qop(m >> 1), m < 2 ? f32x16{} : sn[m & 1]);
+            else o[m & 3] = mfma16(opk, pv_in[((m - 16) >> 2)], o[m & 3]);
             SB();
             if constexpr (k < 4) dma_k(integral_constant<int, k>{});
             else if constexpr (k < 8) dma_v(integral_constant<int, k - 4>{});
