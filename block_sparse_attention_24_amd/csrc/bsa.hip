@@ -24,10 +24,11 @@
 //   * bf16: v_mfma_f32_32x32x16_bf16; fp32: v_mfma_f32_32x32x2f32; fp8 (OCP
 //     E4M3): v_mfma_f32_32x32x64_f8f6f4 with P cast per query and block as
 //     P * 2^e and the E8M0 operand scale undoing 2^e.
-//   * Two kernels.  bsa_fp8_kernel (fp8, d = 128, 128-token blocks) is a
-//     software pipeline that loads K/V straight into LDS; bsa_kernel (all other
-//     shapes) alternates MFMA and softmax phases between the two waves of a
-//     SIMD, with register-staged loads.  Each is described where it is defined.
+//   * Three kernels.  bsa_fp8_kernel (fp8, d = 128, 128-token blocks) and
+//     bsa_bf16_kernel (bf16, same shape) are software pipelines that load K/V
+//     straight into LDS; bsa_kernel (all other shapes) alternates MFMA and
+//     softmax phases between the two waves of a SIMD, with register-staged
+//     loads.  Each is described where it is defined.
 #include <type_traits>
 
 #include "device_common.h"
