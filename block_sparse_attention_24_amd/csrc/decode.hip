@@ -147,8 +147,18 @@ __global__ __launch_bounds__(64) void dec_select_kernel(DecArgs a) {
         key[c] = (j >= 1 && j < I) ? keys[j] : 0u;
     }
     const int nch = (I + 63) >> 6;
-    uint32_t th = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
+    uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int j = c * 64 + lane;
+        if (c < nch && j >= 1 && j < I) {
+            kmin = min(kmin, key[c]);
+            kmax = max(kmax, key[c]);
+        }
+    }
+    int top;
+    uint32_t th = key_prefix(wave_min_u32(kmin), wave_max_u32(kmax), top);   // bits above top: common
+    for (int bit = top; bit >= 0; --bit) {
         const uint32_t cand = th | (1u << bit);
         int cnt = 0;
 #pragma unroll

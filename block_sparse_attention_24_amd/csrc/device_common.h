@@ -70,6 +70,26 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Starting point of a bitwise search for a k-th largest key among keys that
+// all lie in [kmin, kmax]: the bits they share above the highest differing
+// bit, and that bit (-1 when kmin == kmax, in which case the prefix is the key).
+__device__ __forceinline__ uint32_t key_prefix(uint32_t kmin, uint32_t kmax, int &top) {
+    const uint32_t diff = kmin ^ kmax;
+    top = diff ? 31 - __builtin_clz(diff) : -1;
+    return top < 0 ? kmax : (kmin & ~((2u << top) - 1u));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off));
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
+    return x;
+}
+
 // Number of set bits of `m` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));

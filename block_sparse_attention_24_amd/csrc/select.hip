@@ -50,12 +50,25 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
         }
     }
 
-    // Threshold key t: the want-th largest key (bitwise search from the top).
+    // Threshold key t: the want-th largest key, by a bitwise search from the
+    // highest bit on which the row's candidate keys differ (the bits above it
+    // are common to all of them, so to t as well).
     uint32_t t = 0u;
     int need_eq = 0;                           // keys == t still to keep, smallest J first
     const bool all = want >= ncand;
     if (want > 0 && !all) {
-        for (int bit = 31; bit >= 0; --bit) {
+        uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int j = c * 64 + lane;
+            if (c < nch && j >= 1 && j < I) {
+                kmin = min(kmin, key[c]);
+                kmax = max(kmax, key[c]);
+            }
+        }
+        int top;
+        t = key_prefix(wave_min_u32(kmin), wave_max_u32(kmax), top);
+        for (int bit = top; bit >= 0; --bit) {
             const uint32_t cand = t | (1u << bit);
             int cnt = 0;
 #pragma unroll
