@@ -23,6 +23,8 @@ it implements; those readings cannot be checked against the authors and are
 from .stem import (  # noqa: F401
     E4M3_MAX,
     attention_rows,
+    blasst_attention,
+    blasst_attention_rows,
     block_sparse_attention,
     cache_write,
     causal_block_count,

@@ -9,6 +9,9 @@ Sources (web pages; no code exists on them):
              §一.3.1 Token Position Decay, §一.3.2 Output-Aware Metric,
              §二.1 challenges of existing operators, §二.2.1 Stem operator,
              §二.2.2 BSA operator, §二.3 operator benchmark.
+  [BLASST]   "BLASST: Dynamic BLocked Attention Sparsity via Softmax
+             Thresholding" (gist.science summary) — §2.1 running-maximum
+             pruning (the online skip on top of the block mask).
   [Stem-en]  "Tencent Hunyuan introduces Stem sparse attention algorithm"
              (setupai.cc) — "Technical Deep Dive".
 
@@ -390,6 +393,140 @@ def attention_rows(q, k, v, block_mask, block, rows, softmax_scale=None):
         out_o[members] = oo
         out_l[members] = ll
     return out_o, out_l
+
+
+# --------------------------------------------------------------------------
+# Online skip inside the block loop  [BLASST §2.1]
+# --------------------------------------------------------------------------
+
+def _attend_blasst(qrows, pos, kept_blocks, i_blk, block, k_h, v_h, tau, lam):
+    """One query block's rows under the online skip of the BLASST summary
+    (§2.1, running-maximum pruning) applied on top of the block mask.
+
+    The row's kept key blocks are visited in ascending J, as a blocked online
+    softmax visits them, keeping the running maximum m of the logits taken in.
+    For block J the local maximum mt over the keys the row can see is compared
+    with m: if mt - m < ln(lam) the row drops the block (no exponentials, no
+    sum, no product with V).  A dropped block lies below m, so it never moves
+    m, and m before block J is the maximum over every earlier kept block; the
+    first block (m = -inf) is never dropped, and lam = 0 drops nothing.
+    Returns O, LSE (natural log) over the blocks not dropped, the number of
+    blocks each row dropped, and each row's smallest |mt - m - ln(lam)| over
+    its blocks (how close a decision came to the threshold)."""
+    rows = len(pos)
+    log_lam = math.log(lam) if lam > 0 else -math.inf
+    m = np.full(rows, -np.inf)
+    dropped = np.zeros(rows, dtype=np.int64)
+    closest = np.full(rows, np.inf)
+    keys_all, logits_all = [], []
+    for J in kept_blocks:
+        keys = np.arange(J * block, (J + 1) * block)
+        lg = tau * (qrows @ k_h[keys].T)                         # [rows, block]
+        if J == i_blk:                                           # causal inside the diagonal block
+            lg = np.where(keys[None, :] > pos[:, None], -np.inf, lg)
+        mt = lg.max(axis=1)
+        gap = mt - m                                             # +inf before the first block
+        drop = _blasst_drops(gap, log_lam)
+        with np.errstate(invalid="ignore"):
+            margin = np.abs(gap - log_lam)                       # inf when m or ln(lam) is -inf
+        closest = np.minimum(closest, np.where(np.isnan(margin), np.inf, margin))
+        dropped += drop
+        m = np.where(drop, m, np.maximum(m, mt))
+        keys_all.append(keys)
+        logits_all.append(np.where(drop[:, None], -np.inf, lg))
+    if not keys_all:
+        d = qrows.shape[-1]
+        return np.zeros((rows, d)), np.full(rows, -np.inf), dropped, closest
+    keys_idx = np.concatenate(keys_all)
+    logits = np.concatenate(logits_all, axis=1)
+    top = logits.max(axis=1)
+    p = np.exp(logits - top[:, None])
+    l_sum = p.sum(axis=1)
+    o = (p @ v_h[keys_idx]) / l_sum[:, None]
+    return o, top + np.log(l_sum), dropped, closest
+
+
+def _blasst_drops(gap, log_lam):
+    """The skip test of BLASST §2.1: the block's local maximum lies more than
+    ln(1/lam) below the running maximum."""
+    return gap < log_lam
+
+
+def _blasst_check(lam):
+    lam = float(lam)
+    if not (0.0 <= lam <= 1.0):
+        raise ValueError("lam must lie in [0, 1]")
+    return lam
+
+
+def blasst_attention(q, k, v, block_mask, block, lam, softmax_scale=None):
+    """Block-sparse causal attention with the BLASST online skip (see
+    _attend_blasst) inside every row's loop over its kept blocks.
+    block_mask [b, Hq, Nb, Nb] bool, or None for every causal block (the
+    pages' setting: the skip inside dense attention).  Returns O [b, S, Hq, d],
+    LSE [b, Hq, S], dropped [b, Hq, S] and closest [b, Hq, S]."""
+    lam = _blasst_check(lam)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b, S, Hq, d = q.shape
+    group = Hq // k.shape[2]
+    nb = S // block
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = np.zeros((b, S, Hq, d))
+    lse = np.full((b, Hq, S), -np.inf)
+    dropped = np.zeros((b, Hq, S), dtype=np.int64)
+    closest = np.full((b, Hq, S), np.inf)
+    for bi in range(b):
+        for h in range(Hq):
+            g = h // group
+            for i_blk in range(nb):
+                row = np.ones(nb, dtype=bool) if block_mask is None else block_mask[bi, h, i_blk]
+                kept = [j for j in range(i_blk + 1) if row[j]]
+                pos = np.arange(i_blk * block, (i_blk + 1) * block)
+                oo, ll, dd, cc = _attend_blasst(q[bi, pos, h], pos, kept, i_blk, block,
+                                                k[bi, :, g], v[bi, :, g], tau, lam)
+                o[bi, pos, h] = oo
+                lse[bi, h, pos] = ll
+                dropped[bi, h, pos] = dd
+                closest[bi, h, pos] = cc
+    return o, lse, dropped, closest
+
+
+def blasst_attention_rows(q, k, v, block_mask, block, lam, rows, softmax_scale=None):
+    """blasst_attention evaluated only at the (batch, head, token) triples in
+    `rows` (block_mask as for attention_rows).  Returns O [rows, d], LSE,
+    dropped and closest [rows]."""
+    lam = _blasst_check(lam)
+    S, Hq, d = q.shape[1], q.shape[2], q.shape[3]
+    group = Hq // k.shape[2]
+    nb = S // block
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out_o = np.zeros((len(rows), d))
+    out_l = np.zeros(len(rows))
+    out_d = np.zeros(len(rows), dtype=np.int64)
+    out_c = np.zeros(len(rows))
+    groups = {}
+    for n, (bi, h, i) in enumerate(rows):
+        groups.setdefault((bi, h, i // block), []).append(n)
+    for (bi, h, i_blk), members in groups.items():
+        if block_mask is None:
+            mrow = np.ones(nb, dtype=bool)
+        elif callable(block_mask):
+            mrow = block_mask(bi, h, i_blk)
+        else:
+            mrow = block_mask[bi, h, i_blk]
+        kept = [j for j in range(i_blk + 1) if mrow[j]]
+        g = h // group
+        pos = np.array([rows[n][2] for n in members])
+        oo, ll, dd, cc = _attend_blasst(np.asarray(q[bi, pos, h], dtype=np.float64), pos, kept, i_blk,
+                                        block, np.asarray(k[bi, :, g], dtype=np.float64),
+                                        np.asarray(v[bi, :, g], dtype=np.float64), tau, lam)
+        out_o[members] = oo
+        out_l[members] = ll
+        out_d[members] = dd
+        out_c[members] = cc
+    return out_o, out_l, out_d, out_c
 
 
 def decode_step(q, k, v, seq_lens, block, keep=None, softmax_scale=None, value_term=True):

@@ -685,3 +685,191 @@ def test_planted_attention_mistakes_are_caught(monkeypatch):
         o, _ = ostem.block_sparse_attention(q, k, v, full, B)
         assert np.max(np.abs(o - ref)) > 1e-3
     monkeypatch.undo()
+
+
+# --------------------------------------------------------------------------
+# Online skip on top of the mask (BLASST summary §2.1)
+# --------------------------------------------------------------------------
+
+def _blasst_hand_case():
+    """d = 1, softmax scale 1, q = 1 on every row, so a key's logit is its K
+    value.  Blocks of 4 tokens: J0 logits 5, J1 0, J2 6, J3 -2, J4
+    [1.5, 1.5, 9, 9]; V is 10, 20, 30, 40 per block and 50, 60, 70, 80 in J4."""
+    B, nb = 4, 5
+    logit = np.array([5.0] * 4 + [0.0] * 4 + [6.0] * 4 + [-2.0] * 4 + [1.5, 1.5, 9.0, 9.0])
+    val = np.array([10.0] * 4 + [20.0] * 4 + [30.0] * 4 + [40.0] * 4 + [50.0, 60.0, 70.0, 80.0])
+    q = np.ones((1, B * nb, 1, 1))
+    k = logit.reshape(1, -1, 1, 1)
+    v = val.reshape(1, -1, 1, 1)
+    return q, k, v, B, nb
+
+
+def _weighted(pairs):
+    """O and LSE of explicit (count, logit, value) terms."""
+    w = np.array([c * math.exp(x) for c, x, _ in pairs])
+    vals = np.array([val for _, _, val in pairs])
+    return float(w @ vals / w.sum()), math.log(w.sum())
+
+
+def test_blasst_hand_worked_case():
+    """ln(lam) = -4, worked by hand from the rule: a block is dropped when its
+    largest visible logit is more than 4 below the running maximum."""
+    q, k, v, B, nb = _blasst_hand_case()
+    lam = math.exp(-4.0)
+    o, lse, dropped, _ = oracle.blasst_attention(q, k, v, None, B, lam, softmax_scale=1.0)
+    e5, e6 = (4, 5.0, 10.0), (4, 6.0, 30.0)
+    want = {}
+    for i in range(4):                                        # J0 only (diagonal, first): kept
+        want[i] = (_weighted([(i + 1, 5.0, 10.0)]), 0)
+    for i in range(4, 8):                                     # J1 (0 - 5 = -5): dropped
+        want[i] = (_weighted([e5]), 1)
+    for i in range(8, 12):                                    # J2 (6 - 5 = 1): kept
+        want[i] = (_weighted([e5, (i - 7, 6.0, 30.0)]), 1)
+    for i in range(12, 16):                                   # J3 (-2 - 6 = -8): dropped
+        want[i] = (_weighted([e5, e6]), 2)
+    for i in (16, 17):                                        # J4 sees only 1.5: 1.5 - 6 < -4
+        want[i] = (_weighted([e5, e6]), 3)
+    want[18] = (_weighted([e5, e6, (1, 1.5, 50.0), (1, 1.5, 60.0), (1, 9.0, 70.0)]), 2)
+    want[19] = (_weighted([e5, e6, (1, 1.5, 50.0), (1, 1.5, 60.0), (1, 9.0, 70.0), (1, 9.0, 80.0)]), 2)
+    for i, ((oi, li), di) in want.items():
+        assert abs(o[0, i, 0, 0] - oi) < 1e-12 * abs(oi), i
+        assert abs(lse[0, 0, i] - li) < 1e-12, i
+        assert dropped[0, 0, i] == di, i
+
+    # the running maximum covers the mask's kept blocks only: without J2 in
+    # row I = 4, J4's 1.5 is 3.5 below J0's 5 and is kept
+    mask = np.tril(np.ones((1, 1, nb, nb), dtype=bool))
+    mask[0, 0, 4, 2] = False
+    o2, _, d2, _ = oracle.blasst_attention(q, k, v, mask, B, lam, softmax_scale=1.0)
+    for i in (16, 17):
+        terms = [e5] + [(1, 1.5, 50.0 + 10 * t) for t in range(i - 15)]
+        assert abs(o2[0, i, 0, 0] - _weighted(terms)[0]) < 1e-12 * 60, i
+        assert d2[0, 0, i] == 2, i                            # J1 and J3
+
+
+def _blasst_by_prefix_max(q, k, v, mask, B, lam, tau):
+    """The rule restated without a sequential loop: a dropped block never
+    raises the running maximum, so block J is dropped exactly when its local
+    maximum lies more than ln(1/lam) below the largest local maximum of the
+    row's earlier kept blocks.  Attention over the rest comes from torch's
+    SDPA with a boolean mask."""
+    b, S, hq, d = q.shape
+    G = hq // k.shape[2]
+    nb = S // B
+    o = np.zeros_like(q)
+    dropped = np.zeros((b, hq, S), dtype=np.int64)
+    causal = np.tril(np.ones((S, S), dtype=bool))
+    for bi in range(b):
+        for h in range(hq):
+            g = h // G
+            logits = tau * q[bi, :, h] @ k[bi, :, g].T
+            allowed = np.zeros((S, S), dtype=bool)
+            for i in range(S):
+                I = i // B
+                kept = [J for J in range(I + 1) if mask[bi, h, I, J]]
+                local = np.array([logits[i, J * B:min((J + 1) * B, i + 1)].max() for J in kept])
+                before = np.concatenate([[-np.inf], np.maximum.accumulate(local)[:-1]])
+                for J, mt, pm in zip(kept, local, before):
+                    if lam > 0 and mt - pm < math.log(lam):
+                        dropped[bi, h, i] += 1
+                    else:
+                        allowed[i, J * B:(J + 1) * B] = True
+            allowed &= causal
+            qt = torch.from_numpy(q[bi, :, h][None, None])
+            kt = torch.from_numpy(np.ascontiguousarray(k[bi, :, g])[None, None])
+            vt = torch.from_numpy(np.ascontiguousarray(v[bi, :, g])[None, None])
+            out = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(allowed), scale=tau)
+            o[bi, :, h] = out[0, 0].numpy()
+    return o, dropped
+
+
+@pytest.mark.parametrize("lam", [1e-3, 0.05, 0.3, 1.0])
+def test_blasst_equals_prefix_max_rule_with_sdpa(lam):
+    b, S, hq, hkv, d, B = 1, 96, 4, 2, 8, 16
+    q, k, v = _rand_qkv(21, b, S, hq, hkv, d)
+    k[:, :2] *= 3.0                                           # a sink, so that drops happen
+    nb = S // B
+    rng = np.random.default_rng(3)
+    mask = np.tril(rng.random((b, hq, nb, nb)) < 0.6)
+    mask[..., 0] = True
+    mask[:, :, np.arange(nb), np.arange(nb)] = True
+    tau = 1 / math.sqrt(d)
+    o, _, dropped, _ = oracle.blasst_attention(q, k, v, mask, B, lam)
+    o_ref, d_ref = _blasst_by_prefix_max(q, k, v, mask, B, lam, tau)
+    assert np.array_equal(dropped, d_ref)
+    assert np.max(np.abs(o - o_ref)) < 1e-12
+    if lam >= 0.05:
+        assert dropped.sum() > 0
+
+
+def test_blasst_lambda_zero_is_plain_attention():
+    b, S, hq, hkv, d, B = 2, 64, 2, 1, 8, 16
+    q, k, v = _rand_qkv(8, b, S, hq, hkv, d)
+    nb = S // B
+    mask = np.tril(np.random.default_rng(1).random((b, hq, nb, nb)) < 0.5)
+    mask[..., 0] = True
+    mask[:, :, np.arange(nb), np.arange(nb)] = True
+    o, lse, dropped, closest = oracle.blasst_attention(q, k, v, mask, B, 0.0)
+    o_ref, lse_ref = oracle.block_sparse_attention(q, k, v, mask, B)
+    assert not dropped.any() and np.all(np.isinf(closest))
+    assert np.max(np.abs(o - o_ref)) < 1e-12 and np.max(np.abs(lse - lse_ref)) < 1e-12
+
+
+@pytest.mark.parametrize("lam", [1e-4, 1e-2])
+def test_blasst_error_bound(lam):
+    """Every dropped key's weight is below lam relative to the row maximum,
+    which a kept block holds, so O moves by at most 2 lam B n_dropped max|v|."""
+    b, S, hq, hkv, d, B = 1, 128, 2, 2, 16, 16
+    q, k, v = _rand_qkv(4, b, S, hq, hkv, d)
+    k[:, :4] *= 4.0
+    o, _, dropped, _ = oracle.blasst_attention(q, k, v, None, B, lam)
+    o_full, _ = oracle.dense_causal_attention(q, k, v)
+    vmax = np.abs(v).max()
+    bound = 2 * lam * B * dropped * vmax                       # [b, hq, S]
+    err = np.abs(o - o_full).max(axis=3).transpose(0, 2, 1)    # [b, hq, S]
+    assert np.all(err <= bound + 1e-12)
+    assert dropped.sum() > 0
+
+
+def test_blasst_rows_match_full():
+    b, S, hq, hkv, d, B = 1, 96, 4, 2, 8, 16
+    q, k, v = _rand_qkv(6, b, S, hq, hkv, d)
+    k[:, :2] *= 3.0
+    nb = S // B
+    mask = np.tril(np.ones((b, hq, nb, nb), dtype=bool))
+    o, lse, dropped, closest = oracle.blasst_attention(q, k, v, mask, B, 0.1)
+    rows = [(0, 1, 5), (0, 3, 95), (0, 0, 40), (0, 2, 63)]
+    ro, rl, rd, rc = oracle.blasst_attention_rows(q, k, v, mask, B, 0.1, rows)
+    for n, (bi, h, i) in enumerate(rows):
+        assert np.allclose(ro[n], o[bi, i, h], atol=1e-13)
+        assert abs(rl[n] - lse[bi, h, i]) < 1e-13
+        assert rd[n] == dropped[bi, h, i]
+        assert rc[n] == closest[bi, h, i] or abs(rc[n] - closest[bi, h, i]) < 1e-12
+
+
+def test_blasst_rejects_bad_lambda():
+    q, k, v, B, nb = _blasst_hand_case()
+    for lam in (-0.1, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            oracle.blasst_attention(q, k, v, None, B, lam)
+
+
+def test_planted_blasst_mistakes_are_caught(monkeypatch):
+    q, k, v, B, nb = _blasst_hand_case()
+    lam = math.exp(-4.0)
+    want_dropped = np.array([0] * 4 + [1] * 4 + [1] * 4 + [2] * 4 + [3, 3, 2, 2])
+
+    def flipped(gap, log_lam):                      # running max minus block max
+        return -gap < log_lam
+
+    def log2_threshold(gap, log_lam):               # threshold taken in log2 units
+        return gap < log_lam / math.log(2.0)
+
+    for bad in (flipped, log2_threshold):
+        monkeypatch.setattr(ostem, "_blasst_drops", bad)
+        with np.errstate(invalid="ignore"):                 # a mutant may drop a row's every block
+            _, _, dropped, _ = oracle.blasst_attention(q, k, v, None, B, lam, softmax_scale=1.0)
+        assert not np.array_equal(dropped[0, 0], want_dropped)
+    monkeypatch.undo()
+    _, _, dropped, _ = oracle.blasst_attention(q, k, v, None, B, lam, softmax_scale=1.0)
+    assert np.array_equal(dropped[0, 0], want_dropped)
