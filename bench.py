@@ -36,7 +36,8 @@ PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "f32": 157.3}   # MI355X dense MFM
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {w.name: w for w in wl.ALL}
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_24_amd", "csrc", "bsa.hip")
+# the attention kernels and the launcher that runs them on the measured path
+ATTN_SRC = [os.path.join(ROOT, "block_sparse_attention_24_amd", "csrc", f) for f in ("bsa_kernels.h", "bsa.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -47,8 +48,10 @@ def attn_kernel_name(w: wl.Workload) -> str:
 def attn_source_hash() -> str:
     """sha256 of the attention source with comments and whitespace removed, so
     that only a change of the code itself retires a recorded measurement."""
-    with open(ATTN_SRC, encoding="utf-8") as f:
-        code = "".join(line.split("//", 1)[0] for line in f)
+    code = ""
+    for path in ATTN_SRC:
+        with open(path, encoding="utf-8") as f:
+            code += "".join(line.split("//", 1)[0] for line in f)
     return hashlib.sha256("".join(code.split()).encode()).hexdigest()
 
 
@@ -213,6 +216,73 @@ def time_decode(w: wl.Workload, p, k, v, table, page, ws_score, runs: int):
     }
 
 
+def _droppable(w: wl.Workload, mask: torch.Tensor) -> int:
+    """(row, block) pairs the online skip could drop: every kept block of a
+    row except its first (never dropped), summed over rows."""
+    bits = torch.zeros((), dtype=torch.int64, device=mask.device)
+    words = mask.view(torch.int32)
+    for i in range(words.shape[-1]):
+        x = words[..., i].to(torch.int64) & 0xFFFFFFFF
+        for _ in range(32):
+            bits = bits + (x & 1).sum()
+            x = x >> 1
+    return int(bits) * w.block - w.batch * w.hq * w.seq          # bits above the diagonal are zero
+
+
+def time_blasst(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float, lam: float, runs: int):
+    """The attention with BLASST's online skip at threshold lam on top of the
+    Stem mask: time per launch, its ratio to the plain sparse launch, and the
+    share of droppable (row, block) pairs the rows dropped."""
+    dev = "cuda"
+    o = torch.empty((w.batch, w.seq, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.hq, w.seq), dtype=torch.float32, device=dev)
+    skipped = torch.empty((w.batch, w.hq, w.seq), dtype=torch.int32, device=dev)
+    t = Timer()
+    sb.bsa_prefill_blasst(p, q, k, v, mask, lam, o, lse, skipped, table, page)
+    for _ in range(runs):
+        with t:
+            sb.bsa_prefill_blasst(p, q, k, v, mask, lam, o, lse, skipped, table, page)
+    torch.cuda.synchronize()
+    ms = sum(t.ms()) / runs
+    dropped = int(skipped.to(torch.int64).sum())
+    return {"lambda": lam, "ms": ms, "plain_sparse_ms": plain_ms, "speedup": plain_ms / ms,
+            "dropped_share": dropped / max(_droppable(w, mask), 1)}
+
+
+def blasst_report(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float, runs: int):
+    """The online skip on the bench workload itself, and on the same shapes
+    with a sink that every query attends to (sink_logit 12: the situation the
+    skip is made for; the default recipe's random sink is rarely dominant)."""
+    dev = "cuda"
+    rep = {"recipe": [time_blasst(w, p, q, k, v, table, page, mask, plain_ms, lam, runs)
+                      for lam in (1e-3, 1e-2)]}
+    ws_ = dataclasses.replace(w, name=w.name + "-sink12", sink=False, sink_logit=12.0)
+    inp = wl.make_inputs(ws_, device=dev, gen_device=dev)
+    ps = sb.Problem(w.batch, w.seq, w.hq, w.hkv, w.head_dim, w.block, w.dtype,
+                    float(inp["q_scale"]), float(inp["k_scale"]), float(inp["v_scale"]))
+    ks, vs = (inp["k_pages"], inp["v_pages"]) if w.paged else (inp["k"], inp["v"])
+    nb = w.num_blocks
+    scores = torch.empty((w.batch, w.hq, nb, nb), dtype=torch.float32, device=dev)
+    wsb = torch.empty(sb.stem_score_workspace_size(ps), dtype=torch.uint8, device=dev)
+    ms_ = torch.empty_like(mask)
+    sb.stem_score(ps, inp["q"], ks, vs, scores, wsb, table, page)
+    sb.stem_select(ps, scores, w.density, w.alpha, ms_)
+    del scores, wsb
+    o = torch.empty((w.batch, w.seq, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.hq, w.seq), dtype=torch.float32, device=dev)
+    t = Timer()
+    sb.bsa_prefill(ps, inp["q"], ks, vs, ms_, o, lse, table, page)
+    for _ in range(runs):
+        with t:
+            sb.bsa_prefill(ps, inp["q"], ks, vs, ms_, o, lse, table, page)
+    torch.cuda.synchronize()
+    sink_plain = sum(t.ms()) / runs
+    del o, lse
+    rep["sink_logit_12"] = [time_blasst(ws_, ps, inp["q"], ks, vs, table, page, ms_, sink_plain, lam, runs)
+                            for lam in (1e-3, 1e-2)]
+    return rep
+
+
 class Timer:
     """HIP events on the stream the library launches on (torch's current stream)."""
 
@@ -297,6 +367,8 @@ def main():
                     help="skip timing one decode step over the full cache")
     ap.add_argument("--no-cache-write", action="store_true",
                     help="skip timing the fused KV-cache write and scoring from its output")
+    ap.add_argument("--no-blasst", action="store_true",
+                    help="skip timing the attention with BLASST's online skip")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the attention source hash recorded next to measured traffic, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -431,6 +503,10 @@ def main():
     if not args.no_decode:
         log(f"[bench] decode step over the full cache, {args.dense_steps * 10} runs")
         result["decode"] = time_decode(w, p, k, v, table, page, ws, args.dense_steps * 10)
+
+    if not args.no_blasst and (w.head_dim, w.block) == (128, 128) and w.dtype != "f32":
+        log(f"[bench] online skip (BLASST) on the Stem mask, {args.dense_steps} runs each")
+        result["blasst"] = blasst_report(w, p, q, k, v, table, page, mask, bsa_ms, args.dense_steps)
 
     if not args.no_cache_write:
         log(f"[bench] fused KV-cache write and pooled scoring, {args.dense_steps} runs each")

@@ -8,9 +8,9 @@ missing, every call raises.
 Entry points mirror the C names:
   stem_score_workspace_size, stem_score, stem_score_sam, stem_score_pooled,
   stem_cache_write, stem_tpd_budget, stem_select, bsa_prefill,
-  stem_decode_workspace_size, stem_decode, stem_last_error
+  bsa_prefill_blasst, stem_decode_workspace_size, stem_decode, stem_last_error
 plus allocating conveniences ``score``, ``score_pooled``, ``cache_write``,
-``select``, ``attention`` and ``decode``.
+``select``, ``attention``, ``attention_blasst`` and ``decode``.
 """
 
 from __future__ import annotations
@@ -31,7 +31,7 @@ _DTYPES = {"f32": STEM_F32, "bf16": STEM_BF16, "fp8": STEM_FP8_E4M3}
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 EXPORTS = ("stem_score_workspace_size", "stem_score", "stem_score_sam", "stem_score_pooled",
-           "stem_cache_write", "stem_tpd_budget", "stem_select", "bsa_prefill",
+           "stem_cache_write", "stem_tpd_budget", "stem_select", "bsa_prefill", "bsa_prefill_blasst",
            "stem_decode_workspace_size", "stem_decode", "stem_last_error")
 
 
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         h.stem_tpd_budget.argtypes = [I32, D, D, P, ctypes.POINTER(I64)]
         h.stem_select.argtypes = [ctypes.POINTER(AttnDesc), P, D, D, P, P, I32, P, P]
         h.bsa_prefill.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, P, P]
+        h.bsa_prefill_blasst.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, D, P, P, P, P]
         h.stem_decode_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
         h.stem_decode.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, P, P,
                                   P, P, P, SZ, P]
@@ -201,6 +202,14 @@ def bsa_prefill(p: Problem, q, k, v, mask, o, lse=None, block_table=None, page_s
                              _ptr(lse), _stream(stream)))
 
 
+def bsa_prefill_blasst(p: Problem, q, k, v, mask, lam, o, lse=None, skipped=None, block_table=None,
+                       page_size=0, stream=None):
+    d = p.desc()
+    kv = _kv(k, v, block_table, page_size)
+    _check(lib().bsa_prefill_blasst(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(mask), float(lam),
+                                    _ptr(o), _ptr(lse), _ptr(skipped), _stream(stream)))
+
+
 def stem_decode_workspace_size(p: Problem) -> int:
     n = ctypes.c_size_t(0)
     d = p.desc()
@@ -278,6 +287,19 @@ def attention(p: Problem, q, k, v, mask=None, block_table=None, page_size=0, wit
            if with_lse else None)
     bsa_prefill(p, q, k, v, mask, o, lse, block_table, page_size, stream)
     return o, lse
+
+
+def attention_blasst(p: Problem, q, k, v, lam, mask=None, block_table=None, page_size=0,
+                     with_lse=True, stream=None):
+    """Attention with the online skip at threshold lam.  Returns (O, LSE or
+    None, skipped [b, Hq, S] int32: blocks each row dropped)."""
+    odt = torch.bfloat16
+    o = torch.empty((p.batch, p.seq_len, p.num_q_heads, p.head_dim), dtype=odt, device=q.device)
+    lse = (torch.empty((p.batch, p.num_q_heads, p.seq_len), dtype=torch.float32, device=q.device)
+           if with_lse else None)
+    skipped = torch.empty((p.batch, p.num_q_heads, p.seq_len), dtype=torch.int32, device=q.device)
+    bsa_prefill_blasst(p, q, k, v, mask, lam, o, lse, skipped, block_table, page_size, stream)
+    return o, lse, skipped
 
 
 def decode(p: Problem, q, k, v, seq_lens, keep=None, kbar=None, lvn=None, block_table=None,

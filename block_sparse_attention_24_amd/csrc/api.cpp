@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 
 #include "stem_internal.h"
 
@@ -123,6 +124,23 @@ void workspace_layout(const Shape &s, size_t *qbar, size_t *kbar, size_t *lvn, s
 
 // stem_score and stem_score_sam: pool Q, K (and V) into the workspace, then
 // the score GEMM (with the value term unless sam).
+// Arguments of the attention entry points: shapes, K/V, q and o present, and
+// the limits of the attention kernels (32-bit K/V offsets, pages of at least
+// 16 tokens).
+int check_attention(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv, void *o, Shape *s,
+                    KvView *v) {
+    int rc = check_desc(desc, s);
+    if (rc) return rc;
+    if ((rc = check_kv(kv, *s, v))) return rc;
+    if (!q || !o) return fail(STEM_EINVAL, "q or o is NULL");
+    const size_t es = s->dtype == STEM_F32 ? 4 : s->dtype == STEM_BF16 ? 2 : 1;
+    const size_t rows = v->table ? (size_t)kv->num_pages * kv->page_size : (size_t)s->batch * s->seq;
+    if (rows * s->hkv * s->d * es >= (size_t(1) << 32))
+        return fail(STEM_EUNSUPPORTED, "K/V tensors of 4 GiB or more are not supported");
+    if (v->table && kv->page_size < 16) return fail(STEM_EUNSUPPORTED, "page_size below 16 tokens is not supported");
+    return 0;
+}
+
 int score_from_kv(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv, float *scores,
                   void *workspace, size_t workspace_bytes, void *stream, bool sam) {
     Shape s;
@@ -241,22 +259,27 @@ int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *k
                 const uint32_t *mask, void *o, float *lse, void *stream) {
     Shape s;
     KvView v;
-    int rc = check_desc(desc, &s);
+    int rc = check_attention(desc, q, kv, o, &s, &v);
     if (rc) return rc;
-    if ((rc = check_kv(kv, s, &v))) return rc;
-    if (!q || !o) return fail(STEM_EINVAL, "q or o is NULL");
-    {
-        // the attention kernel addresses K and V with 32-bit buffer offsets
-        const size_t es = s.dtype == STEM_F32 ? 4 : s.dtype == STEM_BF16 ? 2 : 1;
-        const size_t rows = v.table ? (size_t)kv->num_pages * kv->page_size : (size_t)s.batch * s.seq;
-        if (rows * s.hkv * s.d * es >= (size_t(1) << 32))
-            return fail(STEM_EUNSUPPORTED, "K/V tensors of 4 GiB or more are not supported");
-        if (v.table && kv->page_size < 16)
-            return fail(STEM_EUNSUPPORTED, "page_size below 16 tokens is not supported");
-    }
     if ((rc = hip_precheck())) return rc;
     hipError_t e = launch_bsa(s, q, v, mask, o, lse, static_cast<hipStream_t>(stream));
     return hip_status(e, "bsa_prefill launch");
+}
+
+int bsa_prefill_blasst(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                       const uint32_t *mask, double lambda, void *o, float *lse, int32_t *skipped,
+                       void *stream) {
+    Shape s;
+    KvView v;
+    int rc = check_attention(desc, q, kv, o, &s, &v);
+    if (rc) return rc;
+    if (!(lambda >= 0.0 && lambda <= 1.0)) return fail(STEM_EINVAL, "lambda must lie in [0, 1]");
+    if (s.d != 128 || s.blk != 128 || s.dtype == STEM_F32)
+        return fail(STEM_EUNSUPPORTED, "the online skip needs head_dim 128, block_size 128 and bf16 or FP8");
+    if ((rc = hip_precheck())) return rc;
+    const float skip_log2 = lambda > 0.0 ? (float)std::log2(lambda) : -std::numeric_limits<float>::infinity();
+    hipError_t e = launch_bsa_skip(s, q, v, mask, skip_log2, o, lse, skipped, static_cast<hipStream_t>(stream));
+    return hip_status(e, "bsa_prefill_blasst launch");
 }
 
 int stem_decode_workspace_size(const stem_attn_desc *desc, size_t *bytes) {

@@ -89,6 +89,12 @@ hipError_t launch_select(const Shape &s, const TpdPlan &plan, const float *score
                          hipStream_t st);
 hipError_t launch_bsa(const Shape &s, const void *q, const KvView &kv, const uint32_t *mask,
                       void *o, float *lse, hipStream_t st);
+// The same attention with the online skip: a row drops a kept block whose
+// largest logit lies more than log2(1/lambda) below its running maximum
+// (skip_log2 = log2(lambda), -inf: never); skipped (nullable) receives the
+// count per query row.  Only head_dim 128, block 128, bf16 or FP8.
+hipError_t launch_bsa_skip(const Shape &s, const void *q, const KvView &kv, const uint32_t *mask,
+                           float skip_log2, void *o, float *lse, int32_t *skipped, hipStream_t st);
 // Decode: workspace offsets (kept lists, counts, split partials) and launch.
 void decode_workspace_layout(const Shape &s, size_t *lists, size_t *counts, size_t *part,
                              size_t *total);

@@ -28,6 +28,8 @@
  *   stem_score_pooled  scoring from those precomputed representations.
  *   stem_decode        one decode step over the cache with Stem block
  *                      selection for the new token.
+ *   bsa_prefill_blasst the attention with BLASST's online skip of blocks far
+ *                      below a row's running maximum, on top of the mask.
  *
  * Conventions for every entry point
  *   - Tensors are row-major, in caller-owned DEVICE memory unless a comment
@@ -240,6 +242,31 @@ int stem_select(const stem_attn_desc *desc, const float *scores, double density,
  *         softmax denominator of tau * q.k (dequantised); NULL to skip. */
 int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
                 const uint32_t *mask, void *o, float *lse, void *stream);
+
+/* bsa_prefill with the online skip of BLASST ("BLASST: Dynamic BLocked
+ * Attention Sparsity via Softmax Thresholding", gist.science summary, §2.1
+ * running-maximum pruning) on top of the mask.  Every row visits its kept
+ * blocks in ascending J, keeping the running maximum m of the logits
+ * tau * q.k it has taken in.  Block J's largest logit over the keys the row
+ * sees is compared with m: when it lies more than ln(1 / lambda) below m, the
+ * row drops the block (no exponentials, no sum, no product with V).  A dropped
+ * block never moves m, so the test is against the largest logit of the row's
+ * earlier kept blocks; a row's first block is never dropped.  O and LSE are
+ * those of the blocks not dropped.  When all 32 rows that one wavefront
+ * holds drop a block, its softmax is not computed at all; K and V are still
+ * loaded in order (the summary's §2.3 prefill design).
+ *   mask:    as for bsa_prefill (NULL: every causal block, the pages' dense
+ *            setting of the skip).
+ *   lambda:  in [0, 1]; 0 drops nothing (the result equals bsa_prefill's up
+ *            to rounding); NaN or values outside are STEM_EINVAL.
+ *   o, lse:  as for bsa_prefill.
+ *   skipped: optional int32 [batch, num_q_heads, seq_len]: blocks each query
+ *            row dropped.  NULL to skip.
+ * Supported: head_dim 128, block_size 128, STEM_BF16 or STEM_FP8_E4M3
+ * (STEM_EUNSUPPORTED otherwise). */
+int bsa_prefill_blasst(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                       const uint32_t *mask, double lambda, void *o, float *lse, int32_t *skipped,
+                       void *stream);
 
 /* Message for the last non-OK return on this thread ("" if none). */
 const char *stem_last_error(void);

@@ -65,6 +65,8 @@ def test_bad_shapes_rejected_everywhere(kw, code):
     assert L.stem_score_sam(ctypes.byref(d), FAKE, ctypes.byref(kv), FAKE, FAKE, 1 << 30, None) == code
     assert L.stem_score_pooled(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == code
     assert L.stem_cache_write(ctypes.byref(d), FAKE, FAKE, ctypes.byref(kv), FAKE, FAKE, None) == code
+    assert L.bsa_prefill_blasst(ctypes.byref(d), FAKE, ctypes.byref(kv), None, 0.1, FAKE, None, None,
+                                None) == code
     assert sb.stem_last_error() != ""
 
 
@@ -186,3 +188,21 @@ def test_tpd_budget_errors():
     with pytest.raises(sb.StemError) as e:
         sb.stem_tpd_budget(8, 0.5, 0.25)
     assert e.value.code == sb.STEM_EUNSUPPORTED
+
+
+def test_blasst_rejects_bad_lambda_unsupported_shapes_and_nulls():
+    L = sb.lib()
+    kv = sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
+    d = _desc()
+    for lam in (-0.1, 1.01, float("nan"), float("inf")):
+        assert L.bsa_prefill_blasst(ctypes.byref(d), FAKE, ctypes.byref(kv), FAKE, lam, FAKE, None, None,
+                                    None) == sb.STEM_EINVAL
+        assert "lambda" in sb.stem_last_error()
+    for kw in (dict(head_dim=64), dict(block_size=64), dict(dtype="f32")):
+        dd = _desc(**kw)
+        assert L.bsa_prefill_blasst(ctypes.byref(dd), FAKE, ctypes.byref(kv), FAKE, 0.1, FAKE, None, None,
+                                    None) == sb.STEM_EUNSUPPORTED
+    assert L.bsa_prefill_blasst(ctypes.byref(d), None, ctypes.byref(kv), FAKE, 0.1, FAKE, None, None,
+                                None) == sb.STEM_EINVAL
+    assert L.bsa_prefill_blasst(ctypes.byref(d), FAKE, ctypes.byref(kv), FAKE, 0.1, None, None, None,
+                                None) == sb.STEM_EINVAL

@@ -12,6 +12,13 @@ rows scaled by 4 (an attention-sink stand-in) where asked; V ~ N(0, 1) with
 every token's V row scaled by exp(N(0, 0.5^2)), one factor per token shared
 by all KV heads.  Cast to the working dtype with round-to-nearest-even; FP8
 inputs are quantised per tensor with scale = amax / 448 (OCP E4M3 range).
+
+A sink that every query attends to (what trained models show at the first
+tokens) is an option: with sink_logit = L > 0, every Q row gains 8 u, with
+u = (1, ..., 1) / sqrt(d), and the first four K rows gain L sqrt(d) / 8 u,
+so that (q . k) / sqrt(d) on those keys is L (1 + N(0, 1) / 8) plus the
+keys' own N(0, 1 + 64 / d) term, while the logits on other keys widen from
+N(0, 1) to N(0, 1 + 64 / d).
 """
 
 from __future__ import annotations
@@ -41,6 +48,7 @@ class Workload:
     page_size: int = 64
     seed: int = 0
     v_sigma: float = 0.5        # V row scale ~ LogNormal(0, v_sigma); 0 gives unit-variance V
+    sink_logit: float = 0.0     # > 0: every query's logit on the first 4 tokens is about this
 
     @property
     def num_blocks(self) -> int:
@@ -51,7 +59,8 @@ class Workload:
                 "q_heads": self.hq, "kv_heads": self.hkv, "head_dim": self.head_dim,
                 "block": self.block, "dtype": self.dtype, "density": self.density,
                 "alpha": self.alpha, "paged_kv": self.paged,
-                "page_size": self.page_size if self.paged else None, "v_sigma": self.v_sigma}
+                "page_size": self.page_size if self.paged else None, "v_sigma": self.v_sigma,
+                "sink_logit": self.sink_logit}
 
 
 # The five workloads of the measurement plan, smallest first.
@@ -83,6 +92,16 @@ def quantize_fp8(x: torch.Tensor):
     return codes, scale
 
 
+def _add_sink_direction(q: Optional[torch.Tensor], k: torch.Tensor, sink_logit: float):
+    """q += 8 u on every row, k[:, :4] += sink_logit * sqrt(d) / 8 * u, with
+    u = (1, ..., 1) / sqrt(d) (in place)."""
+    d = k.shape[-1]
+    u = 1.0 / d ** 0.5
+    if q is not None:
+        q.add_(8.0 * u)
+    k[:, :4].add_(sink_logit * d ** 0.5 / 8.0 * u)
+
+
 def v_row_scale(w: Workload, gen_device: Optional[str] = None) -> torch.Tensor:
     """The per-token V row scales ([b, S], on gen_device) that make_inputs
     applies: exp(v_sigma * N(0, 1)) from seed + 3."""
@@ -106,6 +125,8 @@ def make_inputs(w: Workload, device="cpu", gen_device: Optional[str] = None):
     v.mul_(v_row_scale(w, gd)[:, :, None, None])
     if w.sink:
         k[:, :4].mul_(4.0)
+    if w.sink_logit > 0:
+        _add_sink_direction(q, k, w.sink_logit)
     out = {"q_scale": 1.0, "k_scale": 1.0, "v_scale": 1.0}
     if w.dtype == "f32":
         out.update(q=q, k=k, v=v)
@@ -149,6 +170,8 @@ def make_cache_inputs(w: Workload, device="cpu", gen_device: Optional[str] = Non
     v.mul_(v_row_scale(w, gd)[:, :, None, None])
     if w.sink:
         k[:, :4].mul_(4.0)
+    if w.sink_logit > 0:
+        _add_sink_direction(None, k, w.sink_logit)
     out = {"k_scale": 1.0, "v_scale": 1.0}
     if w.dtype == "f32":
         out.update(k=k, v=v)
