@@ -231,8 +231,9 @@ def _droppable(w: wl.Workload, mask: torch.Tensor) -> int:
 
 def time_blasst(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float, lam: float, runs: int):
     """The attention with BLASST's online skip at threshold lam on top of the
-    Stem mask: time per launch, its ratio to the plain sparse launch, and the
-    share of droppable (row, block) pairs the rows dropped."""
+    mask (None: every causal block): time per launch, its ratio to the same
+    launch without the skip, and the share of droppable (row, block) pairs
+    the rows dropped."""
     dev = "cuda"
     o = torch.empty((w.batch, w.seq, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.hq, w.seq), dtype=torch.float32, device=dev)
@@ -245,14 +246,19 @@ def time_blasst(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float, 
     torch.cuda.synchronize()
     ms = sum(t.ms()) / runs
     dropped = int(skipped.to(torch.int64).sum())
-    return {"lambda": lam, "ms": ms, "plain_sparse_ms": plain_ms, "speedup": plain_ms / ms,
-            "dropped_share": dropped / max(_droppable(w, mask), 1)}
+    nb = w.num_blocks
+    droppable = (_droppable(w, mask) if mask is not None
+                 else w.batch * w.hq * w.block * (nb * (nb + 1) // 2 - nb))
+    return {"lambda": lam, "ms": ms, "without_skip_ms": plain_ms, "speedup": plain_ms / ms,
+            "dropped_share": dropped / max(droppable, 1)}
 
 
 def blasst_report(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float, runs: int):
-    """The online skip on the bench workload itself, and on the same shapes
-    with a sink that every query attends to (sink_logit 12: the situation the
-    skip is made for; the default recipe's random sink is rarely dominant)."""
+    """The online skip on the bench workload's Stem mask, and on the same
+    shapes with a sink that every query attends to (sink_logit 12: the
+    situation the skip is made for; the default recipe's random sink is
+    rarely dominant), there both on the Stem mask and inside dense causal
+    attention (the pages' own setting of the skip)."""
     dev = "cuda"
     rep = {"recipe": [time_blasst(w, p, q, k, v, table, page, mask, plain_ms, lam, runs)
                       for lam in (1e-3, 1e-2)]}
@@ -277,9 +283,18 @@ def blasst_report(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float
             sb.bsa_prefill(ps, inp["q"], ks, vs, ms_, o, lse, table, page)
     torch.cuda.synchronize()
     sink_plain = sum(t.ms()) / runs
+    t = Timer()
+    sb.bsa_prefill(ps, inp["q"], ks, vs, None, o, lse, table, page)
+    for _ in range(runs):
+        with t:
+            sb.bsa_prefill(ps, inp["q"], ks, vs, None, o, lse, table, page)
+    torch.cuda.synchronize()
+    sink_dense = sum(t.ms()) / runs
     del o, lse
     rep["sink_logit_12"] = [time_blasst(ws_, ps, inp["q"], ks, vs, table, page, ms_, sink_plain, lam, runs)
                             for lam in (1e-3, 1e-2)]
+    rep["sink_logit_12_dense"] = [time_blasst(ws_, ps, inp["q"], ks, vs, table, page, None, sink_dense, lam, runs)
+                                  for lam in (1e-3, 1e-2)]
     return rep
 
 

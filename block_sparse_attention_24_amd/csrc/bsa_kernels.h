@@ -985,9 +985,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     sync_vm<10, true>();                                   // K(0) and K(1) have landed
 #pragma unroll
     for (int t = 0; t < 2; ++t) s[t] = mfma8(kop(KST, t, 1), qop(1), mfma8(kop(KST, t, 0), qop(0), f32x16{}, 127), 127);
-    // first K operand of S(1), read a block ahead (with the skip, whose state
-    // takes the registers, it is read after the barrier instead)
-    i32x8 kfirst = SKIP ? i32x8{} : kop(KST + TILE, 0, 0);
+    i32x8 kfirst = kop(KST + TILE, 0, 0);                  // first K operand of S(1)
 
     // causal mask inside the diagonal block: keys past this lane's query
     auto mask_diag = [&](f32x16(&x)[2]) {
@@ -1074,13 +1072,6 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
                 mask_diag(sc);
             }
         }
-        bool skip = false;
-        if constexpr (SKIP) {
-            const float xb = fmaxf(hmine, hother) * c;     // block j's max for this row, log2 units
-            skip = xb < pmax + a.skip_log2;
-            pmax = fmaxf(pmax, xb);
-            nskip += skip ? 1 : 0;
-        }
         // ---- the region, in a fixed order: every MFMA is followed by a slice of
         // the softmax of block j, and every LDS operand is read one MFMA ahead.
         // The loads of K(j+4) and V(j+2) into LDS are spread over it, so that
@@ -1089,11 +1080,20 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         auto dma_k = [&](auto I) { load_lds16<KDM + 8 * decltype(I)::value * D>(krs, lds_wave, (unsigned)dk[I], so_k); };
         auto dma_v = [&](auto I) { load_lds16<VDM + 8 * decltype(I)::value * D>(vrs, lds_wave, (unsigned)dv[I], so_v); };
 #define SB() __builtin_amdgcn_sched_barrier(0)
-        // soft: some row of the wave keeps block j (always, without the skip);
-        // the softmax slices are branched over, wave-uniformly, when none does
-        const bool soft = SKIP ? !__all(skip) : true;
-        i32x8 ka = SKIP ? kop(KRD, 0, 0) : kfirst, kb = kop(KRD, 1, 0);
+        i32x8 ka = kfirst, kb = kop(KRD, 1, 0);
         i32x8 va = vop(VRD, 0);
+        // the decision, after the first operand reads so that their latency and
+        // the other half's maximum overlap; soft: some row of the wave keeps
+        // block j (always, without the skip); the softmax slices are branched
+        // over, wave-uniformly, when none does
+        bool skip = false;
+        if constexpr (SKIP) {
+            const float xb = fmaxf(hmine, hother) * c;     // block j's max for this row, log2 units
+            skip = xb < pmax + a.skip_log2;
+            pmax = fmaxf(pmax, xb);
+            nskip += skip ? 1 : 0;
+        }
+        const bool soft = SKIP ? !__all(skip) : true;
         // row max: a tree of three-input maxima (v_max3), 16 for the 32 scores
         auto max3 = [](float x, float y, float z) { return fmaxf(x, fmaxf(y, z)); };
         auto tile_max = [&](const f32x16 &x, float &u, float &v) {
@@ -1161,7 +1161,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         SB();
         sn[1] = mfma8(kb, qop(1), sn[1], 127);
         SB();
-        if constexpr (!SKIP) kfirst = kop(KST + ((R + 2) % NST) * TILE, 0, 0);  // K(j+2): the first operand of S(j+2)
+        kfirst = kop(KST + ((R + 2) % NST) * TILE, 0, 0);  // K(j+2): the first operand of S(j+2)
         dma_v(integral_constant<int, 1>{});
         expq(0, 8);
         packq(1);
@@ -1531,13 +1531,6 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
                 mask_diag(sc);
             }
         }
-        bool skip = false;
-        if constexpr (SKIP) {
-            const float xb = fmaxf(hmine, hother) * c;     // block j's max for this row, log2 units
-            skip = xb < pmax + a.skip_log2;
-            pmax = fmaxf(pmax, xb);
-            nskip += skip ? 1 : 0;
-        }
 #define SB() __builtin_amdgcn_sched_barrier(0)
         auto dma_k = [&](auto I) {
             load_lds16<KDM + 4 * decltype(I)::value * ROWB>(krs, lds_wave, (unsigned)dk[I], so_k);
@@ -1550,9 +1543,6 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
             u = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8]));
             v = max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]);
         };
-        // soft: some row of the wave keeps block j (always, without the skip);
-        // the softmax work is branched over, wave-uniformly, when none does
-        const bool soft = SKIP ? !__all(skip) : true;
         float ls[4];
         float Me = M;                                      // exp2 offset: +inf for a dropped row
         auto expq = [&](int t, int e0) {                   // P of 4 scores, into the partial sums
@@ -1581,6 +1571,18 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
             return vop(VRD, (m - 16) >> 3, ((m - 16) >> 2) & 1, m & 3);
         };
         bf16x8 opk = operand(order(0));
+        // the decision, after the first operand read so that its latency and
+        // the other half's maximum overlap; soft: some row of the wave keeps
+        // block j (always, without the skip); the softmax work is branched
+        // over, wave-uniformly, when none does
+        bool skip = false;
+        if constexpr (SKIP) {
+            const float xb = fmaxf(hmine, hother) * c;     // block j's max for this row, log2 units
+            skip = xb < pmax + a.skip_log2;
+            pmax = fmaxf(pmax, xb);
+            nskip += skip ? 1 : 0;
+        }
+        const bool soft = SKIP ? !__all(skip) : true;
         float m0, m1, m2, m3, mx = 0.0f;
         auto slot = [&](auto KK) {
             constexpr int k = decltype(KK)::value;
