@@ -29,6 +29,7 @@ from .stem import (  # noqa: F401
     cache_write,
     causal_block_count,
     decode_step,
+    decode_step_blasst,
     dense_causal_attention,
     dequantize,
     e4m3fn_round,

@@ -529,29 +529,11 @@ def blasst_attention_rows(q, k, v, block_mask, block, lam, rows, softmax_scale=N
     return out_o, out_l, out_d, out_c
 
 
-def decode_step(q, k, v, seq_lens, block, keep=None, softmax_scale=None, value_term=True):
-    """One decode step with Stem block selection for the new token.
-
-    q [b, Hq, d]: the new token of each sequence; k, v [b, S, Hkv, d]: the
-    cache (dequantised), sequence b holding tokens 0 .. seq_lens[b]-1 with the
-    new token last, at t = seq_lens[b] - 1 in block I = t // block.
-    The token scores the complete blocks J in [1, I-1] as OAM does a query
-    block (Stem-cn §一.3.2, the token standing for its block's mean), with the
-    block representations of pool_blocks; keep[b] blocks are kept by the rule
-    of select_row (sink and own block forced), keep clamped to
-    [|{0, I}|, I + 1]; keep None keeps every block.  Attention then sees the
-    keys j <= t of the kept blocks (as in _attend).
-    Returns (o [b, Hq, d], lse [b, Hq], kept) with kept[b][h] the sorted
-    kept blocks."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+def _decode_kept(q, k, v, seq_lens, block, keep, tau, value_term):
+    """The kept blocks of each new token's row (sorted), by the rule of
+    decode_step."""
     b, Hq, d = q.shape
-    Hkv = k.shape[2]
-    group = Hq // Hkv
-    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    o = np.zeros((b, Hq, d))
-    lse = np.zeros((b, Hq))
+    group = Hq // k.shape[2]
     kept = []
     for bi in range(b):
         t = int(seq_lens[bi]) - 1
@@ -573,16 +555,77 @@ def decode_step(q, k, v, seq_lens, block, keep=None, softmax_scale=None, value_t
                     if value_term:
                         row[1:I] += lvn[0, g, 1:I]
                 row_kept = select_row(row, I, budget)
-            kept_b.append(row_kept)
+            kept_b.append(list(row_kept))
+        kept.append(kept_b)
+    return kept
+
+
+def decode_step(q, k, v, seq_lens, block, keep=None, softmax_scale=None, value_term=True):
+    """One decode step with Stem block selection for the new token.
+
+    q [b, Hq, d]: the new token of each sequence; k, v [b, S, Hkv, d]: the
+    cache (dequantised), sequence b holding tokens 0 .. seq_lens[b]-1 with the
+    new token last, at t = seq_lens[b] - 1 in block I = t // block.
+    The token scores the complete blocks J in [1, I-1] as OAM does a query
+    block (Stem-cn §一.3.2, the token standing for its block's mean), with the
+    block representations of pool_blocks; keep[b] blocks are kept by the rule
+    of select_row (sink and own block forced), keep clamped to
+    [|{0, I}|, I + 1]; keep None keeps every block.  Attention then sees the
+    keys j <= t of the kept blocks (as in _attend).
+    Returns (o [b, Hq, d], lse [b, Hq], kept) with kept[b][h] the sorted
+    kept blocks."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b, Hq, d = q.shape
+    group = Hq // k.shape[2]
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    kept = _decode_kept(q, k, v, seq_lens, block, keep, tau, value_term)
+    o = np.zeros((b, Hq, d))
+    lse = np.zeros((b, Hq))
+    for bi in range(b):
+        t = int(seq_lens[bi]) - 1
+        I = t // block
+        for h in range(Hq):
+            g = h // group
             mrow = np.zeros(I + 1, dtype=bool)
-            mrow[row_kept] = True
+            mrow[kept[bi][h]] = True
             keys_idx, diag = _visible_keys(mrow, I, block)
             oo, ll = _attend(q[bi, h][None, :], np.array([t]), keys_idx, diag, I, block,
                              k[bi, :, g], v[bi, :, g], tau)
             o[bi, h] = oo[0]
             lse[bi, h] = ll[0]
-        kept.append(kept_b)
     return o, lse, kept
+
+
+def decode_step_blasst(q, k, v, seq_lens, block, lam, keep=None, softmax_scale=None, value_term=True):
+    """decode_step with the online skip of BLASST §2.1 (see _attend_blasst)
+    over the new token's kept blocks, in ascending J: a block whose largest
+    logit over the keys j <= t lies more than ln(1/lam) below the largest of
+    the earlier kept blocks is dropped.  (BLASST §2.3 names decode, where the
+    skip saves the dropped blocks' V reads.)  Returns (o [b, Hq, d],
+    lse [b, Hq], kept, dropped [b, Hq], closest [b, Hq])."""
+    lam = _blasst_check(lam)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b, Hq, d = q.shape
+    group = Hq // k.shape[2]
+    tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    kept = _decode_kept(q, k, v, seq_lens, block, keep, tau, value_term)
+    o = np.zeros((b, Hq, d))
+    lse = np.zeros((b, Hq))
+    dropped = np.zeros((b, Hq), dtype=np.int64)
+    closest = np.zeros((b, Hq))
+    for bi in range(b):
+        t = int(seq_lens[bi]) - 1
+        I = t // block
+        for h in range(Hq):
+            g = h // group
+            oo, ll, dd, cc = _attend_blasst(q[bi, h][None, :], np.array([t]), kept[bi][h], I, block,
+                                            k[bi, :, g], v[bi, :, g], tau, lam)
+            o[bi, h], lse[bi, h], dropped[bi, h], closest[bi, h] = oo[0], ll[0], dd[0], cc[0]
+    return o, lse, kept, dropped, closest
 
 
 def dense_causal_attention(q, k, v, softmax_scale=None):

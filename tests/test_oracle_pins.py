@@ -582,6 +582,53 @@ def test_decode_equals_prefill_row_of_a_constant_query_block(t, keep):
         assert abs(lse[0, h] - lse_p[0, h, t]) < 1e-12
 
 
+@pytest.mark.parametrize("t,keep,lam", [(16 * 5 + 3, 3, 0.05), (16 * 6 - 1, 4, 0.5), (16 * 7, None, 0.3),
+                                        (16 * 6 + 8, 7, 1.0), (5, 3, 0.5), (16 * 8 - 1, None, 1e-3)])
+def test_decode_blasst_equals_prefill_row_of_a_constant_query_block(t, keep, lam):
+    """As for decode_step: a query block of copies of the new token makes the
+    prefill row at t keep the same blocks, and the online skip then drops the
+    same blocks there (it depends only on that row's logits)."""
+    rng = np.random.default_rng(t + 100)
+    b, hq, hkv, d, B = 1, 4, 2, 8, 16
+    I = t // B
+    S = (I + 1) * B
+    k = rng.standard_normal((b, S, hkv, d))
+    k[:, :2] *= 3.0
+    v = rng.standard_normal((b, S, hkv, d)) * np.exp(rng.standard_normal((b, S, 1, 1)))
+    q_full = rng.standard_normal((b, S, hq, d))
+    qt = rng.standard_normal((b, hq, d))
+    q_full[0, I * B:(I + 1) * B] = qt[0]
+    o, lse, kept, dropped, _ = oracle.decode_step_blasst(qt, k, v, [t + 1], B, lam,
+                                                         keep=None if keep is None else [keep])
+    nb = I + 1
+    if keep is None:
+        mask = np.tril(np.ones((b, hq, nb, nb), dtype=bool))
+    else:
+        s = oracle.oam_scores(q_full, k, v, B)
+        budget = [1] + [2] * I
+        budget[I] = min(max(keep, 1 if I == 0 else 2), I + 1)
+        mask = oracle.select_blocks(s, budget)
+    o_p, lse_p, d_p, _ = oracle.blasst_attention(q_full, k, v, mask, B, lam)
+    for h in range(hq):
+        assert kept[0][h] == list(np.nonzero(mask[0, h, I])[0])
+        assert dropped[0, h] == d_p[0, h, t]
+        assert np.max(np.abs(o[0, h] - o_p[0, t, h])) < 1e-12
+        assert abs(lse[0, h] - lse_p[0, h, t]) < 1e-12
+
+
+def test_decode_blasst_lambda_zero_is_decode_step():
+    rng = np.random.default_rng(9)
+    b, hq, hkv, d, B, S = 2, 4, 2, 8, 16, 16 * 9
+    k = rng.standard_normal((b, S, hkv, d))
+    v = rng.standard_normal((b, S, hkv, d))
+    qt = rng.standard_normal((b, hq, d))
+    lens = [S, 16 * 5 + 7]
+    o, lse, kept = oracle.decode_step(qt, k, v, lens, B, keep=[4, 3])
+    o2, lse2, kept2, dropped, _ = oracle.decode_step_blasst(qt, k, v, lens, B, 0.0, keep=[4, 3])
+    assert kept == kept2 and not dropped.any()
+    assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - lse2)) < 1e-12
+
+
 # --------------------------------------------------------------------------
 # FP8 E4M3 rounding
 # --------------------------------------------------------------------------
