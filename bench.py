@@ -216,6 +216,41 @@ def time_decode(w: wl.Workload, p, k, v, table, page, ws_score, runs: int):
     }
 
 
+def time_decode_pair(w: wl.Workload, p, q, k, v, table, page, kbar, lvn, lam: float, runs: int):
+    """One decode step over the full cache (the new token at the last
+    position, row Nb-1's TPD budget) with and without the online skip: ms of
+    each, the blocks dropped per row, and the V bytes the dropped blocks
+    did not read."""
+    dev = "cuda"
+    nb = w.num_blocks
+    budget, _ = sb.stem_tpd_budget(nb, w.density, w.alpha)
+    lens = torch.full((w.batch,), w.seq, dtype=torch.int32, device=dev)
+    keep = torch.full((w.batch,), budget[nb - 1], dtype=torch.int32, device=dev)
+    o = torch.empty((w.batch, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device=dev)
+    skipped = torch.empty((w.batch, w.hq), dtype=torch.int32, device=dev)
+    ws0 = torch.empty(sb.stem_decode_workspace_size(p), dtype=torch.uint8, device=dev)
+    ws1 = torch.empty(sb.stem_decode_blasst_workspace_size(p), dtype=torch.uint8, device=dev)
+    plain = lambda: sb.stem_decode(p, q, k, v, lens, keep, kbar, lvn, o, lse, ws0, table, page)
+    skip = lambda: sb.stem_decode_blasst(p, q, k, v, lens, keep, kbar, lvn, lam, o, lse, skipped, ws1,
+                                         table, page)
+    res = {}
+    for name, fn in (("decode_ms", plain), ("decode_skip_ms", skip)):
+        t = Timer()
+        fn()
+        for _ in range(runs):
+            with t:
+                fn()
+        torch.cuda.synchronize()
+        res[name] = sum(t.ms()) / runs
+    es = {"bf16": 2, "fp8": 1}[w.dtype]
+    dropped = float(skipped.to(torch.float64).mean())
+    res.update({"lambda": lam, "kept_blocks_per_row": budget[nb - 1], "dropped_blocks_per_row": dropped,
+                "v_bytes_not_read": int(skipped.to(torch.int64).sum()) * w.block * w.head_dim * es,
+                "speedup": res["decode_ms"] / res["decode_skip_ms"]})
+    return res
+
+
 def _droppable(w: wl.Workload, mask: torch.Tensor) -> int:
     """(row, block) pairs the online skip could drop: every kept block of a
     row except its first (never dropped), summed over rows."""
@@ -253,15 +288,27 @@ def time_blasst(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float, 
             "dropped_share": dropped / max(droppable, 1)}
 
 
-def blasst_report(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float, runs: int):
+def blasst_report(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float, runs: int, ws_score=None):
     """The online skip on the bench workload's Stem mask, and on the same
     shapes with a sink that every query attends to (sink_logit 12: the
     situation the skip is made for; the default recipe's random sink is
     rarely dominant), there both on the Stem mask and inside dense causal
-    attention (the pages' own setting of the skip)."""
+    attention (the pages' own setting of the skip).  Also a decode step over
+    each cache with and without the skip (ws_score: the workspace stem_score
+    left, whose block representations the decode step scores with)."""
     dev = "cuda"
     rep = {"recipe": [time_blasst(w, p, q, k, v, table, page, mask, plain_ms, lam, runs)
                       for lam in (1e-3, 1e-2)]}
+    if ws_score is not None:
+        al = lambda x: (x + 255) // 256 * 256
+        nb = w.num_blocks
+        nq = w.batch * w.hq * nb * w.head_dim * 4
+        nk = w.batch * w.hkv * nb * w.head_dim * 4
+        kbar = ws_score[al(nq):al(nq) + nk].view(torch.float32).view(w.batch, w.hkv, nb, w.head_dim)
+        lvn = ws_score[al(nq) + al(nk):al(nq) + al(nk) + w.batch * w.hkv * nb * 4].view(torch.float32)
+        qd, qds = wl.make_decode_query(w, w.seed + 7, dev)
+        pd = dataclasses.replace(p, q_scale=qds)
+        rep["decode_recipe"] = time_decode_pair(w, pd, qd, k, v, table, page, kbar, lvn, 1e-3, runs * 10)
     ws_ = dataclasses.replace(w, name=w.name + "-sink12", sink=False, sink_logit=12.0)
     inp = wl.make_inputs(ws_, device=dev, gen_device=dev)
     ps = sb.Problem(w.batch, w.seq, w.hq, w.hkv, w.head_dim, w.block, w.dtype,
@@ -273,7 +320,16 @@ def blasst_report(w: wl.Workload, p, q, k, v, table, page, mask, plain_ms: float
     ms_ = torch.empty_like(mask)
     sb.stem_score(ps, inp["q"], ks, vs, scores, wsb, table, page)
     sb.stem_select(ps, scores, w.density, w.alpha, ms_)
-    del scores, wsb
+    del scores
+    # decode over this cache, with the block representations stem_score pooled
+    al = lambda x: (x + 255) // 256 * 256
+    nq = w.batch * w.hq * nb * w.head_dim * 4
+    nk = w.batch * w.hkv * nb * w.head_dim * 4
+    kbar = wsb[al(nq):al(nq) + nk].view(torch.float32).view(w.batch, w.hkv, nb, w.head_dim)
+    lvn = wsb[al(nq) + al(nk):al(nq) + al(nk) + w.batch * w.hkv * nb * 4].view(torch.float32)
+    qd, qds = wl.make_decode_query(ws_, w.seed + 7, dev)
+    pd = dataclasses.replace(ps, q_scale=qds)
+    rep["decode_sink_logit_12"] = time_decode_pair(ws_, pd, qd, ks, vs, table, page, kbar, lvn, 1e-3, runs * 10)
     o = torch.empty((w.batch, w.seq, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.hq, w.seq), dtype=torch.float32, device=dev)
     t = Timer()
@@ -521,7 +577,7 @@ def main():
 
     if not args.no_blasst and (w.head_dim, w.block) == (128, 128) and w.dtype != "f32":
         log(f"[bench] online skip (BLASST) on the Stem mask, {args.dense_steps} runs each")
-        result["blasst"] = blasst_report(w, p, q, k, v, table, page, mask, bsa_ms, args.dense_steps)
+        result["blasst"] = blasst_report(w, p, q, k, v, table, page, mask, bsa_ms, args.dense_steps, ws)
 
     if not args.no_cache_write:
         log(f"[bench] fused KV-cache write and pooled scoring, {args.dense_steps} runs each")

@@ -8,9 +8,10 @@ missing, every call raises.
 Entry points mirror the C names:
   stem_score_workspace_size, stem_score, stem_score_sam, stem_score_pooled,
   stem_cache_write, stem_tpd_budget, stem_select, bsa_prefill,
-  bsa_prefill_blasst, stem_decode_workspace_size, stem_decode, stem_last_error
+  bsa_prefill_blasst, stem_decode_workspace_size, stem_decode,
+  stem_decode_blasst_workspace_size, stem_decode_blasst, stem_last_error
 plus allocating conveniences ``score``, ``score_pooled``, ``cache_write``,
-``select``, ``attention``, ``attention_blasst`` and ``decode``.
+``select``, ``attention``, ``attention_blasst``, ``decode`` and ``decode_blasst``.
 """
 
 from __future__ import annotations
@@ -32,7 +33,8 @@ _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3
 
 EXPORTS = ("stem_score_workspace_size", "stem_score", "stem_score_sam", "stem_score_pooled",
            "stem_cache_write", "stem_tpd_budget", "stem_select", "bsa_prefill", "bsa_prefill_blasst",
-           "stem_decode_workspace_size", "stem_decode", "stem_last_error")
+           "stem_decode_workspace_size", "stem_decode", "stem_decode_blasst_workspace_size",
+           "stem_decode_blasst", "stem_last_error")
 
 
 class StemError(RuntimeError):
@@ -80,6 +82,9 @@ def lib() -> ctypes.CDLL:
         h.stem_decode_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
         h.stem_decode.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, P, P,
                                   P, P, P, SZ, P]
+        h.stem_decode_blasst_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
+        h.stem_decode_blasst.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, P, P, D,
+                                         P, P, P, P, SZ, P]
         h.stem_last_error.argtypes = []
         h.stem_last_error.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
@@ -226,6 +231,23 @@ def stem_decode(p: Problem, q, k, v, seq_lens, keep, kbar, lvn, o, lse, workspac
                              workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def stem_decode_blasst_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    d = p.desc()
+    _check(lib().stem_decode_blasst_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def stem_decode_blasst(p: Problem, q, k, v, seq_lens, keep, kbar, lvn, lam, o, lse, skipped, workspace,
+                       block_table=None, page_size=0, stream=None):
+    d = p.desc()
+    kv = _kv(k, v, block_table, page_size)
+    _check(lib().stem_decode_blasst(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(seq_lens), _ptr(keep),
+                                    _ptr(kbar), _ptr(lvn), float(lam), _ptr(o), _ptr(lse), _ptr(skipped),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
+
+
 def stem_last_error() -> str:
     return lib().stem_last_error().decode()
 
@@ -312,3 +334,17 @@ def decode(p: Problem, q, k, v, seq_lens, keep=None, kbar=None, lvn=None, block_
     ws = torch.empty(stem_decode_workspace_size(p), dtype=torch.uint8, device=q.device)
     stem_decode(p, q, k, v, seq_lens, keep, kbar, lvn, o, lse, ws, block_table, page_size, stream)
     return o, lse
+
+
+def decode_blasst(p: Problem, q, k, v, seq_lens, lam, keep=None, kbar=None, lvn=None, block_table=None,
+                  page_size=0, stream=None):
+    """One decode step with the online skip at threshold lam.  Returns
+    (O [b, Hq, d], LSE [b, Hq], skipped [b, Hq] int32)."""
+    odt = torch.float32 if p.dtype == "f32" else torch.bfloat16
+    o = torch.empty((p.batch, p.num_q_heads, p.head_dim), dtype=odt, device=q.device)
+    lse = torch.empty((p.batch, p.num_q_heads), dtype=torch.float32, device=q.device)
+    skipped = torch.empty((p.batch, p.num_q_heads), dtype=torch.int32, device=q.device)
+    ws = torch.empty(stem_decode_blasst_workspace_size(p), dtype=torch.uint8, device=q.device)
+    stem_decode_blasst(p, q, k, v, seq_lens, keep, kbar, lvn, lam, o, lse, skipped, ws, block_table, page_size,
+                       stream)
+    return o, lse, skipped

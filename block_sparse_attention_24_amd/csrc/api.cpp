@@ -312,4 +312,39 @@ int stem_decode(const stem_attn_desc *desc, const void *q, const stem_kv_desc *k
     return hip_status(e, "stem_decode launch");
 }
 
+int stem_decode_blasst_workspace_size(const stem_attn_desc *desc, size_t *bytes) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if (!bytes) return fail(STEM_EINVAL, "bytes is NULL");
+    size_t a, b, c, d;
+    decode_skip_layout(s, &a, &b, &c, &d, bytes);
+    return ok();
+}
+
+int stem_decode_blasst(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                       const int32_t *seq_lens, const int32_t *keep, const float *kbar, const float *lvn,
+                       double lambda, void *o, float *lse, int32_t *skipped, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    Shape s;
+    KvView v;
+    int rc = check_desc(desc, &s);
+    if (rc) return rc;
+    if ((rc = check_kv(kv, s, &v))) return rc;
+    if (!q || !seq_lens || !o || !workspace) return fail(STEM_EINVAL, "q, seq_lens, o or workspace is NULL");
+    if (keep && !kbar) return fail(STEM_EINVAL, "kbar is NULL but keep is given");
+    if (!(lambda >= 0.0 && lambda <= 1.0)) return fail(STEM_EINVAL, "lambda must lie in [0, 1]");
+    size_t a, b, c, d, total;
+    decode_skip_layout(s, &a, &b, &c, &d, &total);
+    if (workspace_bytes < total)
+        return fail(STEM_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
+    if ((rc = hip_precheck())) return rc;
+    DecodeSkip sk;
+    sk.log2_lambda = lambda > 0.0 ? (float)std::log2(lambda) : -std::numeric_limits<float>::infinity();
+    sk.skipped = skipped;
+    hipError_t e = launch_decode(s, q, v, seq_lens, keep, kbar, lvn, o, lse, workspace,
+                                 static_cast<hipStream_t>(stream), &sk);
+    return hip_status(e, "stem_decode_blasst launch");
+}
+
 }  // extern "C"

@@ -20,6 +20,21 @@
 //                       merged in wave order.
 //   dec_combine_kernel  one workgroup per (b, h) merges the splits (four
 //                       contiguous quarters, then the quarters in order).
+// With BLASST's online skip (gist.science summary, §2.1 running-maximum
+// pruning; §2.3: in decode the skip saves the V loads) the attention runs in
+// two passes around a scan, so that the V rows of a dropped block are never
+// read:
+//   dec_attn_kernel<QK> each wave reads its block's K rows and writes the
+//                       block's scores and their maximum (log2 units);
+//   dec_prefix_kernel   one wave per (b, h): in ascending J, a block is
+//                       dropped when its maximum lies more than
+//                       log2(1/lambda) below the largest maximum of the
+//                       earlier kept blocks; the entries not dropped are
+//                       listed in order;
+//   dec_attn_kernel<PV> split-K over that list: each wave forms P from its
+//                       block's stored scores and reads the block's V rows
+//                       (workgroups past the list exit at once), and
+//                       dec_combine_kernel merges those splits.
 // Every sum has a fixed order, so results are bit-reproducible.
 #include "device_common.h"
 #include "stem_internal.h"
@@ -28,6 +43,7 @@ namespace stem {
 namespace {
 
 constexpr int kSplit = 4;             // kept blocks per attention workgroup (one per wave)
+enum { kFull = 0, kQK = 1, kPV = 2 };    // attention passes (kQK, kPV: with the online skip)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Orders LDS traffic between the lanes of one wave (no workgroup barrier).
@@ -50,6 +66,13 @@ struct DecArgs {
     uint32_t *keys;                   // [b, hq, nb] order keys of the candidate scores
     void *o;                          // [b, hq, d]
     float *lse;                       // [b, hq] or null
+    // online skip only
+    float *bmax;                      // [b, hq, nb] maximum score of each kept entry (log2 units)
+    float *scores;                    // [b, hq, nb, blk] its scores (log2 units)
+    int32_t *live;                    // [b, hq, nb] the entries not dropped, ascending
+    int32_t *nlive;                   // [b, hq] their number
+    int32_t *skipped;                 // [b, hq] dropped entries, or null
+    float skip_log2;                  // log2(lambda)
     int hq, hkv, d, blk, nb, seq, nsplit;
     float q_scale, k_scale, v_scale, tau;
 };
@@ -192,13 +215,13 @@ __global__ __launch_bounds__(64) void dec_select_kernel(DecArgs a) {
 // ---------------------------------------------------------------------------
 // Split-K attention over the kept blocks
 // ---------------------------------------------------------------------------
-template <int ES, int D, int BLK>
+template <int ES, int D, int BLK, int MODE>
 __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
     constexpr int CPR = D * ES / 16;                // 16-byte chunks per K/V row
     constexpr int RPP = kWave / CPR;                // rows per pass
     constexpr int EPC = 16 / ES;                    // elements per chunk
     constexpr int NP = BLK / RPP;                   // passes over the block's rows
-    constexpr int TOT = 2 * NP;                     // K passes, then V passes
+    constexpr int TOT = MODE == kFull ? 2 * NP : NP;   // K passes, then V passes (or one of them)
     constexpr int DIST = TOT < 8 ? TOT : 8;         // loads in flight per lane
     __shared__ float ps[kSplit][BLK];               // scores, then P, of each wave's block
     __shared__ float ml[kSplit][2];
@@ -217,10 +240,12 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
     const int g = bg % a.hkv, b = bg / a.hkv;
     const int h = g * G + hh;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int count = a.counts[(size_t)b * a.hq + h];
+    // the PV pass walks the entries that were not dropped
+    const int count = MODE == kPV ? a.nlive[(size_t)b * a.hq + h] : a.counts[(size_t)b * a.hq + h];
     if (s * kSplit >= count) return;                // the whole workgroup exits together
     const int t = seq_len_of(a, b) - 1;
-    const int e = s * kSplit + wave;                // this wave's entry of the kept list
+    const int slot = s * kSplit + wave;             // this wave's place in the list it walks
+    const int e = MODE == kPV ? (slot < count ? a.live[((size_t)b * a.hq + h) * a.nb + slot] : 0) : slot;
     const int r = lane / CPR, c = lane % CPR;       // row within a pass, chunk within the row
     const size_t row_bytes = (size_t)a.hkv * D * ES;
     const size_t col = (size_t)g * D * ES + (size_t)c * 16;
@@ -230,8 +255,10 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
     float acc[EPC];
 #pragma unroll
     for (int i = 0; i < EPC; ++i) acc[i] = 0.0f;
+    const size_t ent = ((size_t)b * a.hq + h) * a.nb + e;   // this wave's entry in the skip arrays
+    const bool live = slot < count;
 
-    if (e < count) {
+    if (live) {
         const int J = a.lists[((size_t)b * a.hq + h) * a.nb + e];
         const int tok0 = J * BLK;
         const int nkeys = min(BLK, t - tok0 + 1);
@@ -262,9 +289,31 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
                 roff[p] = ((size_t)b * a.seq + tok) * row_bytes + col;
             }
         }
+        if constexpr (MODE == kPV) {
+            // the scores the QK pass stored, and the block softmax in log2 units
+            const float *sc = a.scores + ent * BLK;
+#pragma unroll
+            for (int k = lane; k < BLK; k += kWave) ps[wave][k] = sc[k];
+            wave_sync();
+            const float mx = a.bmax[ent];
+            float lsum = 0.0f;
+#pragma unroll
+            for (int k = lane; k < BLK; k += kWave) {
+                const float p = __builtin_amdgcn_exp2f(ps[wave][k] - mx);   // 0 for -inf
+                ps[wave][k] = p;
+                lsum += p;
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+            m_w = mx;
+            l_w = lsum;
+            wave_sync();
+        }
+        // pass i reads K rows for i < NP (V rows after them); the PV pass reads V only
+        auto src_of = [&](int i) { return MODE == kPV ? a.v : (i < NP ? a.k : a.v); };
         uint4 ring[DIST];
         auto issue = [&](int i) {
-            ring[i % DIST] = *reinterpret_cast<const uint4 *>((i < NP ? a.k : a.v) + roff[i % NP]);
+            ring[i % DIST] = *reinterpret_cast<const uint4 *>(src_of(i) + roff[i % NP]);
         };
 #pragma unroll
         for (int i = 0; i < DIST; ++i) issue(i);
@@ -273,7 +322,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
             const uint4 u = ring[i % DIST];
             if (i + DIST < TOT) issue(i + DIST);
             const int row = (i % NP) * RPP + r;
-            if (i < NP) {
+            if (MODE != kPV && i < NP) {
                 // scores: one chunk per lane, reduced over the row's CPR lanes
                 float kx[EPC];
                 widen16<ES>(u, kx);
@@ -284,7 +333,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
                 for (int off = 1; off < CPR; off <<= 1) x += __shfl_xor(x, off);
                 if (c == 0) ps[wave][row] = row < nkeys ? x : ninf;
             } else {
-                if (i == NP) {
+                if (MODE == kFull && i == NP) {
                     // block softmax in log2 units
                     wave_sync();
                     float mx = ninf;
@@ -313,11 +362,25 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
                 for (int k = 0; k < EPC; ++k) acc[k] = fmaf(p, vx[k], acc[k]);
             }
         }
+        if constexpr (MODE == kQK) {
+            // the block's scores and their maximum, for the scan and the PV pass
+            wave_sync();
+            float mx = ninf;
+#pragma unroll
+            for (int k = lane; k < BLK; k += kWave) mx = fmaxf(mx, ps[wave][k]);
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            float *sc = a.scores + ent * BLK;
+#pragma unroll
+            for (int k = lane; k < BLK; k += kWave) sc[k] = ps[wave][k];
+            if (lane == 0) a.bmax[ent] = mx;
+        }
 #pragma unroll
         for (int off = CPR; off < kWave; off <<= 1)
 #pragma unroll
             for (int k = 0; k < EPC; ++k) acc[k] += __shfl_xor(acc[k], off);
     }
+    if constexpr (MODE == kQK) return;
     if (lane < CPR) {
 #pragma unroll
         for (int i = 0; i < EPC; ++i) os[wave][lane * EPC + i] = acc[i];
@@ -351,6 +414,45 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
     }
 }
 
+// Online skip, one wave per (b, h): entry e of the kept list (ascending J)
+// is dropped when its maximum lies more than log2(1/lambda) below the largest
+// maximum of entries 0 .. e-1 (a dropped entry lies below it, so it never
+// raises that maximum); entry 0 is never dropped.  A wave takes 64 entries
+// at a time: an inclusive max-scan over the lanes, shifted by one lane, plus
+// the maximum carried from the entries before.
+__global__ __launch_bounds__(64) void dec_prefix_kernel(DecArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const size_t bh = (size_t)b * a.hq + h;
+    const int n = a.counts[bh];
+    const float ninf = -__builtin_huge_valf();
+    const float *mx = a.bmax + bh * a.nb;
+    int32_t *live = a.live + bh * a.nb;
+    float carry = ninf;
+    int dropped = 0, kept = 0;
+    for (int e0 = 0; e0 < n; e0 += kWave) {
+        const int e = e0 + lane;
+        const float x = e < n ? mx[e] : ninf;
+        float inc = x;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float y = __shfl_up(inc, off);
+            if (lane >= off) inc = fmaxf(inc, y);
+        }
+        float before = __shfl_up(inc, 1);
+        before = lane == 0 ? carry : fmaxf(carry, before);   // maximum of entries 0 .. e-1
+        const bool d = e < n && x < before + a.skip_log2;
+        const uint64_t keepm = ballot64(e < n && !d);
+        if (e < n && !d) live[kept + lanes_below(keepm)] = e;   // in ascending order
+        kept += __popcll(keepm);
+        dropped += __popcll(ballot64(d));
+        carry = fmaxf(carry, __shfl(inc, kWave - 1));
+    }
+    if (lane == 0) {
+        a.nlive[bh] = kept;
+        if (a.skipped) a.skipped[bh] = dropped;
+    }
+}
+
 // One workgroup per (b, h): merge the splits.  Each of the four waves sums
 // a contiguous quarter of the splits in order; the quarters are then added
 // in wave order.  Split weights 2^(m_s - M) go through LDS.
@@ -362,7 +464,7 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecArgs a, int out_f32
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const size_t bh = (size_t)b * a.hq + h;
-    const int ns = (a.counts[bh] + kSplit - 1) / kSplit;
+    const int ns = ((a.nlive ? a.nlive[bh] : a.counts[bh]) + kSplit - 1) / kSplit;
     const float *src = a.part + bh * a.nsplit * (D + 2);
     const float ninf = -__builtin_huge_valf();
     float m = ninf;
@@ -407,7 +509,7 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecArgs a, int out_f32
 }
 
 template <int ES, int D, int BLK>
-hipError_t launch_all(const Shape &s, DecArgs &a, hipStream_t st) {
+hipError_t launch_all(const Shape &s, DecArgs &a, bool skip, hipStream_t st) {
     const dim3 heads(s.hq, s.batch);
     const int chunks = (s.nb + 63) / 64;
     hipLaunchKernelGGL((dec_score_kernel<ES, D>), dim3((s.nb + kScoreRows - 1) / kScoreRows, s.hq, s.batch),
@@ -417,14 +519,21 @@ hipError_t launch_all(const Shape &s, DecArgs &a, hipStream_t st) {
     else if (chunks <= 16) hipLaunchKernelGGL((dec_select_kernel<16>), heads, dim3(64), 0, st, a);
     else if (chunks <= 32) hipLaunchKernelGGL((dec_select_kernel<32>), heads, dim3(64), 0, st, a);
     else hipLaunchKernelGGL((dec_select_kernel<64>), heads, dim3(64), 0, st, a);
-    hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK>), dim3(a.nsplit, s.hq, s.batch), dim3(256), 0, st, a);
+    const dim3 splits(a.nsplit, s.hq, s.batch);
+    if (skip) {
+        hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kQK>), splits, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(dec_prefix_kernel, heads, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kPV>), splits, dim3(256), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kFull>), splits, dim3(256), 0, st, a);
+    }
     hipLaunchKernelGGL((dec_combine_kernel<D>), heads, dim3(256), 0, st, a, ES == 4 ? 1 : 0);
     return hipGetLastError();
 }
 
 template <int ES, int D>
-hipError_t launch_blk(const Shape &s, DecArgs &a, hipStream_t st) {
-    return s.blk == 64 ? launch_all<ES, D, 64>(s, a, st) : launch_all<ES, D, 128>(s, a, st);
+hipError_t launch_blk(const Shape &s, DecArgs &a, bool skip, hipStream_t st) {
+    return s.blk == 64 ? launch_all<ES, D, 64>(s, a, skip, st) : launch_all<ES, D, 128>(s, a, skip, st);
 }
 
 }  // namespace
@@ -440,9 +549,22 @@ void decode_workspace_layout(const Shape &s, size_t *lists, size_t *counts, size
     *total = *part + al(bh * nsplit * (s.d + 2) * sizeof(float)) + al(bh * s.nb * sizeof(uint32_t));
 }
 
+void decode_skip_layout(const Shape &s, size_t *bmax, size_t *live, size_t *nlive, size_t *scores,
+                        size_t *total) {
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t bh = (size_t)s.batch * s.hq;
+    size_t l, c, p, base;
+    decode_workspace_layout(s, &l, &c, &p, &base);
+    *bmax = base;
+    *live = *bmax + al(bh * s.nb * sizeof(float));
+    *nlive = *live + al(bh * s.nb * sizeof(int32_t));
+    *scores = *nlive + al(bh * sizeof(int32_t));
+    *total = *scores + al(bh * s.nb * s.blk * sizeof(float));
+}
+
 hipError_t launch_decode(const Shape &s, const void *q, const KvView &kv, const int32_t *seq_lens,
                          const int32_t *keep, const float *kbar, const float *lvn, void *o,
-                         float *lse, void *workspace, hipStream_t st) {
+                         float *lse, void *workspace, hipStream_t st, const DecodeSkip *skip) {
     size_t ol, oc, op, total;
     decode_workspace_layout(s, &ol, &oc, &op, &total);
     char *ws = static_cast<char *>(workspace);
@@ -474,17 +596,28 @@ hipError_t launch_decode(const Shape &s, const void *q, const KvView &kv, const 
     a.k_scale = s.k_scale;
     a.v_scale = s.v_scale;
     a.tau = s.tau;
+    if (skip) {
+        size_t obm, olv, onl, osc, tot2;
+        decode_skip_layout(s, &obm, &olv, &onl, &osc, &tot2);
+        a.bmax = reinterpret_cast<float *>(ws + obm);
+        a.live = reinterpret_cast<int32_t *>(ws + olv);
+        a.nlive = reinterpret_cast<int32_t *>(ws + onl);
+        a.scores = reinterpret_cast<float *>(ws + osc);
+        a.skipped = skip->skipped;
+        a.skip_log2 = skip->log2_lambda;
+    }
+    const bool sk = skip != nullptr;
     if (s.d == 64) {
         switch (s.dtype) {
-            case STEM_F32: return launch_blk<4, 64>(s, a, st);
-            case STEM_BF16: return launch_blk<2, 64>(s, a, st);
-            default: return launch_blk<1, 64>(s, a, st);
+            case STEM_F32: return launch_blk<4, 64>(s, a, sk, st);
+            case STEM_BF16: return launch_blk<2, 64>(s, a, sk, st);
+            default: return launch_blk<1, 64>(s, a, sk, st);
         }
     }
     switch (s.dtype) {
-        case STEM_F32: return launch_blk<4, 128>(s, a, st);
-        case STEM_BF16: return launch_blk<2, 128>(s, a, st);
-        default: return launch_blk<1, 128>(s, a, st);
+        case STEM_F32: return launch_blk<4, 128>(s, a, sk, st);
+        case STEM_BF16: return launch_blk<2, 128>(s, a, sk, st);
+        default: return launch_blk<1, 128>(s, a, sk, st);
     }
 }
 

@@ -98,8 +98,16 @@ hipError_t launch_bsa_skip(const Shape &s, const void *q, const KvView &kv, cons
 // Decode: workspace offsets (kept lists, counts, split partials) and launch.
 void decode_workspace_layout(const Shape &s, size_t *lists, size_t *counts, size_t *part,
                              size_t *total);
+// With the online skip: block maxima, the list of entries not dropped and its
+// length, and the block scores, after the decode workspace.
+void decode_skip_layout(const Shape &s, size_t *bmax, size_t *live, size_t *nlive, size_t *scores,
+                        size_t *total);
+struct DecodeSkip {
+    float log2_lambda;                // -inf: never drop
+    int32_t *skipped;                 // [b, hq] dropped blocks per row, or null
+};
 hipError_t launch_decode(const Shape &s, const void *q, const KvView &kv, const int32_t *seq_lens,
                          const int32_t *keep, const float *kbar, const float *lvn, void *o,
-                         float *lse, void *workspace, hipStream_t st);
+                         float *lse, void *workspace, hipStream_t st, const DecodeSkip *skip = nullptr);
 
 }  // namespace stem

@@ -30,6 +30,8 @@
  *                      selection for the new token.
  *   bsa_prefill_blasst the attention with BLASST's online skip of blocks far
  *                      below a row's running maximum, on top of the mask.
+ *   stem_decode_blasst the decode step with the same skip, which leaves the
+ *                      dropped blocks' V rows unread.
  *
  * Conventions for every entry point
  *   - Tensors are row-major, in caller-owned DEVICE memory unless a comment
@@ -201,6 +203,32 @@ int stem_decode_workspace_size(const stem_attn_desc *desc, size_t *bytes);
 int stem_decode(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
                 const int32_t *seq_lens, const int32_t *keep, const float *kbar, const float *lvn,
                 void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace of stem_decode_blasst: that of stem_decode followed by, each
+ * 256-byte aligned, the kept blocks' maxima fp32 [batch, num_q_heads, Nb]
+ * (entry e = e-th kept block), the entries not dropped int32
+ * [batch, num_q_heads, Nb] in ascending order, their number int32
+ * [batch, num_q_heads], and the kept blocks' scores fp32
+ * [batch, num_q_heads, Nb, block_size]. */
+int stem_decode_blasst_workspace_size(const stem_attn_desc *desc, size_t *bytes);
+
+/* stem_decode with BLASST's online skip ("BLASST: Dynamic BLocked Attention
+ * Sparsity via Softmax Thresholding", gist.science summary: §2.1
+ * running-maximum pruning; §2.3 decode, where skipping a block saves its V
+ * loads).  Among the new token's kept blocks, in ascending J, a block is
+ * dropped when its largest logit tau * q.k over the keys j <= t lies more than
+ * ln(1 / lambda) below the largest of the earlier kept blocks; the first kept
+ * block never is.  O and LSE are those of the blocks not dropped.  The K rows
+ * of every kept block are read; the V rows of a dropped block are not.
+ *   lambda:  in [0, 1] (0 drops nothing); NaN or values outside are
+ *            STEM_EINVAL.
+ *   skipped: optional int32 [batch, num_q_heads]: blocks each row dropped.
+ *   workspace: at least stem_decode_blasst_workspace_size() bytes.
+ * Every other argument, and every check, as for stem_decode. */
+int stem_decode_blasst(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                       const int32_t *seq_lens, const int32_t *keep, const float *kbar, const float *lvn,
+                       double lambda, void *o, float *lse, int32_t *skipped, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* TPD budget on the host (Stem article §一.3.1; setupai.cc "Technical Deep
  * Dive").  T = floor(density * Nb(Nb+1)/2 + 1/2) computed in double, clamped

@@ -206,3 +206,20 @@ def test_blasst_rejects_bad_lambda_unsupported_shapes_and_nulls():
                                 None) == sb.STEM_EINVAL
     assert L.bsa_prefill_blasst(ctypes.byref(d), FAKE, ctypes.byref(kv), FAKE, 0.1, None, None, None,
                                 None) == sb.STEM_EINVAL
+
+
+def test_decode_blasst_checks():
+    L = sb.lib()
+    kv = sb.KvDesc(0x1000, 0x1000, None, 0, 0, 0)
+    p = sb.Problem(1, 1024, 4, 2, 128, 128, "bf16")
+    d = p.desc()
+    n = sb.stem_decode_blasst_workspace_size(p)
+    assert n > sb.stem_decode_workspace_size(p)
+    args = lambda q=FAKE, lens=FAKE, keep=None, kbar=None, lam=0.1, o=FAKE, ws=FAKE, nbytes=n: (
+        ctypes.byref(d), q, ctypes.byref(kv), lens, keep, kbar, None, lam, o, None, None, ws, nbytes, None)
+    for kw in (dict(q=None), dict(lens=None), dict(o=None), dict(ws=None), dict(keep=FAKE)):
+        assert L.stem_decode_blasst(*args(**kw)) == sb.STEM_EINVAL, kw
+    for lam in (-1e-3, 1.5, float("nan")):
+        assert L.stem_decode_blasst(*args(lam=lam)) == sb.STEM_EINVAL
+        assert "lambda" in sb.stem_last_error()
+    assert L.stem_decode_blasst(*args(nbytes=n - 1)) == sb.STEM_EWORKSPACE

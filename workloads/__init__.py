@@ -193,6 +193,19 @@ def make_cache_inputs(w: Workload, device="cpu", gen_device: Optional[str] = Non
     return out
 
 
+def make_decode_query(w: Workload, seed: int, device="cpu"):
+    """The new token's query of a decode step over workload w's cache:
+    q [b, Hq, d] ~ N(0, 1) from `seed` (plus the sink direction 8 u when
+    sink_logit > 0), in the working dtype; returns (q, q_scale)."""
+    q = torch.randn((w.batch, w.hq, w.head_dim), generator=_gen(seed, "cpu"), dtype=torch.float32)
+    if w.sink_logit > 0:
+        q.add_(8.0 / w.head_dim ** 0.5)
+    if w.dtype == "fp8":
+        codes, scale = quantize_fp8(q)
+        return codes.to(device), float(scale)
+    return (q.to(torch.bfloat16) if w.dtype == "bf16" else q).to(device), 1.0
+
+
 def to_float64(x: torch.Tensor):
     """Exact upcast of a working-dtype tensor (fp8 codes included) to a float64
     numpy array.  Per-tensor scales are applied by the consumer."""
