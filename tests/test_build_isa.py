@@ -17,7 +17,8 @@ import tempfile
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OBJ = os.path.join(ROOT, "block_sparse_attention_24_amd", "_build", "bsa.o")
+# the attention kernels without and with the online skip
+OBJS = [os.path.join(ROOT, "block_sparse_attention_24_amd", "_build", f) for f in ("bsa.o", "bsa_skip.o")]
 LLVM = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin")
 
 
@@ -35,13 +36,14 @@ def _disassemble(obj: str) -> list[str]:
     return [ln.split("//")[0].strip() for ln in out.splitlines() if ln.startswith("\t")]
 
 
-def test_m0_written_only_by_the_lds_loads():
-    if not os.path.exists(OBJ):
+@pytest.mark.parametrize("obj", OBJS, ids=os.path.basename)
+def test_m0_written_only_by_the_lds_loads(obj):
+    if not os.path.exists(obj):
         pytest.skip("attention object not built (python -m block_sparse_attention_24_amd.build)")
     if not all(os.path.exists(os.path.join(LLVM, t)) for t in ("llvm-objcopy", "clang-offload-bundler",
                                                                   "llvm-objdump")):
         pytest.skip("LLVM tools not found")
-    ins = _disassemble(OBJ)
+    ins = _disassemble(obj)
     assert ins, "empty disassembly"
     ours = re.compile(r"^s_add_u32 m0, s\d+, (0x[0-9a-f]+|\d+)$")
     writes = 0
