@@ -125,6 +125,20 @@ def test_lambda_zero_is_bsa_prefill(case):
     assert int(skipped.abs().sum()) == 0
 
 
+def test_blasst_run_twice_bit_identical():
+    w = CASES[1][0]
+    _announce(f"blasst twice {w.name}")
+    inp = wl.make_inputs(w, device=DEV)
+    p = problem(w, inp)
+    k, v, table, page = kv_args(w, inp)
+    s, _ = sb.score(p, inp["q"], k, v, table, page)
+    words, _, _ = sb.select(p, s, w.density, w.alpha)
+    r1 = sb.attention_blasst(p, inp["q"], k, v, 0.2, words, table, page)
+    r2 = sb.attention_blasst(p, inp["q"], k, v, 0.2, words, table, page)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(r1, r2))
+
+
 def test_blasst_empty_rows_and_null_outputs():
     """A user mask with empty rows: O = 0, LSE = -inf, nothing dropped; the
     optional outputs may be NULL."""

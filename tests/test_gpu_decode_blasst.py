@@ -181,6 +181,16 @@ def test_decode_blasst_lambda_zero_is_stem_decode(case):
     assert int(skipped.abs().sum()) == 0
 
 
+def test_decode_blasst_run_twice_bit_identical():
+    case = CASES[3]
+    w = case.w
+    _announce(f"decode blasst twice {w.name}")
+    s = _setup(w, case.lens, case.keep)
+    r1 = _decode(w, s, 1e-3)
+    r2 = _decode(w, s, 1e-3)
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
+
+
 def test_decode_blasst_full_128k_sampled_groups():
     """128K tokens, 64/8 heads, fp8 paged: the new token at the last position
     of a full cache, the TPD budget, lambda = 1e-3; two KV groups against the
