@@ -8,8 +8,9 @@
 // no HBM traffic).
 //
 // Kernels:
-//   dec_score_kernel    the candidates' scores, as order-preserving keys,
-//                       256 rows per workgroup.
+//   dec_score_kernel    the candidates' scores, as order-preserving keys:
+//                       64 rows of one KV head per workgroup, scored for
+//                       every query head of its group.
 //   dec_select_kernel   one wave per (b, h) finds the top-k by a bitwise
 //                       search for the k-th largest key (equal scores to the
 //                       smaller J) and writes the kept list in ascending J.
@@ -109,42 +110,57 @@ __device__ __forceinline__ RowPlan row_plan(const DecArgs &a, int b) {
 
 // Scores of the candidates J in [1, I-1]: a row of kbar is read by D/4 lanes
 // (one 16-byte piece each), so a wave covers 256/D rows per load, U loads in
-// flight per lane; the dot product is finished by a butterfly over the row's
-// lanes.  A workgroup scores kScoreRows rows of one (b, h).
-constexpr int kScoreRows = 256;
+// flight per lane.  A workgroup scores kScoreRows rows of one KV head for
+// every query head of its group: each kbar row is read once, and for each
+// head the dot product is finished by a butterfly over the row's lanes.
+constexpr int kScoreRows = 64;
+constexpr int kScoreHeads = 64;                      // query heads staged in LDS at a time
 template <int ES, int D>
 __global__ __launch_bounds__(256) void dec_score_kernel(DecArgs a) {
     constexpr int LPR = D / 4;                      // lanes per kbar row
     constexpr int RPW = kWave / LPR;                // rows per wave and load
     constexpr int STEP = 4 * RPW;                   // rows per workgroup and load
     constexpr int U = kScoreRows / STEP;            // loads per lane
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.y, b = blockIdx.z;
     const RowPlan rp = row_plan(a, b);
     const int j0 = 1 + blockIdx.x * kScoreRows;
     if (rp.want >= rp.ncand || j0 >= rp.I) return;  // no selection, or no rows here
     const int I = rp.I;
-    const int g = h / (a.hq / a.hkv);
+    const int G = a.hq / a.hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int sub = lane / LPR, piece = lane % LPR;
-    f32x4 qv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qv[i] = q_elem<ES>(a, ((size_t)b * a.hq + h) * D + 4 * piece + i);
     const float *kb = a.kbar + ((size_t)b * a.hkv + g) * a.nb * D + 4 * piece;
     const float *lv = a.lvn ? a.lvn + ((size_t)b * a.hkv + g) * a.nb : nullptr;
-    uint32_t *keys = a.keys + ((size_t)b * a.hq + h) * a.nb;
+    __shared__ f32x4 qs[kScoreHeads * (D / 4)];    // the group's queries, dequantised
     f32x4 x[U];
+    float lj[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int jc = min(j0 + u * STEP + wave * RPW + sub, I - 1);   // past the end: a valid row
         x[u] = *reinterpret_cast<const f32x4 *>(kb + (size_t)jc * D);
+        lj[u] = lv ? lv[jc] : 0.0f;
     }
+    for (int h0 = 0; h0 < G; h0 += kScoreHeads) {
+        const int nh = min(kScoreHeads, G - h0);
+        if (h0 > 0) __syncthreads();                // the previous heads' queries are read
+        for (int i = tid; i < nh * (D / 4); i += 256) {
+            const size_t base = ((size_t)b * a.hq + g * G + h0 + i / (D / 4)) * D + 4 * (i % (D / 4));
+            qs[i] = f32x4{q_elem<ES>(a, base), q_elem<ES>(a, base + 1), q_elem<ES>(a, base + 2),
+                          q_elem<ES>(a, base + 3)};
+        }
+        __syncthreads();
+        for (int hh = 0; hh < nh; ++hh) {
+            const int h = g * G + h0 + hh;
+            const f32x4 qv = qs[hh * (D / 4) + piece];
+            uint32_t *keys = a.keys + ((size_t)b * a.hq + h) * a.nb;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * STEP + wave * RPW + sub;
-        float acc = fmaf(qv[3], x[u][3], fmaf(qv[2], x[u][2], fmaf(qv[1], x[u][1], qv[0] * x[u][0])));
-#pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-        if (piece == 0 && j < I) keys[j] = order_key(fmaf(acc, a.tau, lv ? lv[j] : 0.0f));
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + u * STEP + wave * RPW + sub;
+                const float acc =
+                    sum_lanes<LPR>(fmaf(qv[3], x[u][3], fmaf(qv[2], x[u][2], fmaf(qv[1], x[u][1], qv[0] * x[u][0]))));
+                if (piece == 0 && j < I) keys[j] = order_key(fmaf(acc, a.tau, lj[u]));
+            }
+        }
     }
 }
 
@@ -303,8 +319,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
                 ps[wave][k] = p;
                 lsum += p;
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+            lsum = sum_lanes<kWave>(lsum);
             m_w = mx;
             l_w = lsum;
             wave_sync();
@@ -329,8 +344,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
                 float x = 0.0f;
 #pragma unroll
                 for (int k = 0; k < EPC; ++k) x = fmaf(qv[k], kx[k], x);
-#pragma unroll
-                for (int off = 1; off < CPR; off <<= 1) x += __shfl_xor(x, off);
+                x = sum_lanes<CPR>(x);
                 if (c == 0) ps[wave][row] = row < nkeys ? x : ninf;
             } else {
                 if (MODE == kFull && i == NP) {
@@ -339,8 +353,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
                     float mx = ninf;
 #pragma unroll
                     for (int k = lane; k < BLK; k += kWave) mx = fmaxf(mx, ps[wave][k]);
-#pragma unroll
-                    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+                    mx = max_lanes<kWave>(mx);
                     float lsum = 0.0f;
 #pragma unroll
                     for (int k = lane; k < BLK; k += kWave) {
@@ -348,8 +361,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
                         ps[wave][k] = p;
                         lsum += p;
                     }
-#pragma unroll
-                    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+                    lsum = sum_lanes<kWave>(lsum);
                     m_w = mx;
                     l_w = lsum;
                     wave_sync();
@@ -368,17 +380,14 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
             float mx = ninf;
 #pragma unroll
             for (int k = lane; k < BLK; k += kWave) mx = fmaxf(mx, ps[wave][k]);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            mx = max_lanes<kWave>(mx);
             float *sc = a.scores + ent * BLK;
 #pragma unroll
             for (int k = lane; k < BLK; k += kWave) sc[k] = ps[wave][k];
             if (lane == 0) a.bmax[ent] = mx;
         }
 #pragma unroll
-        for (int off = CPR; off < kWave; off <<= 1)
-#pragma unroll
-            for (int k = 0; k < EPC; ++k) acc[k] += __shfl_xor(acc[k], off);
+        for (int k = 0; k < EPC; ++k) acc[k] = sum_stride<CPR>(acc[k]);
     }
     if constexpr (MODE == kQK) return;
     if (lane < CPR) {
@@ -469,8 +478,7 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecArgs a, int out_f32
     const float ninf = -__builtin_huge_valf();
     float m = ninf;
     for (int s = tid; s < ns; s += 256) m = fmaxf(m, src[(size_t)s * (D + 2)]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    m = max_lanes<kWave>(m);
     if (lane == 0) mred[wave] = m;
     __syncthreads();
     const float M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
@@ -512,7 +520,7 @@ template <int ES, int D, int BLK>
 hipError_t launch_all(const Shape &s, DecArgs &a, bool skip, hipStream_t st) {
     const dim3 heads(s.hq, s.batch);
     const int chunks = (s.nb + 63) / 64;
-    hipLaunchKernelGGL((dec_score_kernel<ES, D>), dim3((s.nb + kScoreRows - 1) / kScoreRows, s.hq, s.batch),
+    hipLaunchKernelGGL((dec_score_kernel<ES, D>), dim3((s.nb + kScoreRows - 1) / kScoreRows, s.hkv, s.batch),
                        dim3(256), 0, st, a);
     if (chunks <= 2) hipLaunchKernelGGL((dec_select_kernel<2>), heads, dim3(64), 0, st, a);
     else if (chunks <= 8) hipLaunchKernelGGL((dec_select_kernel<8>), heads, dim3(64), 0, st, a);

@@ -61,6 +61,56 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Reductions across lanes on the VALU (DPP within 16-lane rows,
+// v_permlane16_swap / v_permlane32_swap across rows), so that no step takes
+// an LDS round trip.  Every lane of a group receives the same result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum_xor16(float x) {       // x of lanes l and l ^ 16
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum / max over each aligned group of N consecutive lanes (N a power of two
+// up to 64).  Pairs: lanes l ^ 1, l ^ 2 (quad permutes), then the halves of
+// 8 and of 16 lanes (mirrors, which pair the same partial sums as l ^ 4 and
+// l ^ 8), then l ^ 16 and l ^ 32.
+template <int N>
+__device__ __forceinline__ float sum_lanes(float x) {
+    if constexpr (N >= 2) x += dpp_f32<0xB1>(x);             // quad_perm [1, 0, 3, 2]
+    if constexpr (N >= 4) x += dpp_f32<0x4E>(x);             // quad_perm [2, 3, 0, 1]
+    if constexpr (N >= 8) x += dpp_f32<0x141>(x);            // row_half_mirror
+    if constexpr (N >= 16) x += dpp_f32<0x140>(x);           // row_mirror
+    if constexpr (N >= 32) x = sum_xor16(x);
+    if constexpr (N >= 64) x = sum_xor32(x);
+    return x;
+}
+template <int N>
+__device__ __forceinline__ float max_lanes(float x) {
+    if constexpr (N >= 2) x = fmaxf(x, dpp_f32<0xB1>(x));
+    if constexpr (N >= 4) x = fmaxf(x, dpp_f32<0x4E>(x));
+    if constexpr (N >= 8) x = fmaxf(x, dpp_f32<0x141>(x));
+    if constexpr (N >= 16) x = fmaxf(x, dpp_f32<0x140>(x));
+    if constexpr (N >= 32) x = max_xor16(x);
+    if constexpr (N >= 64) x = max_xor32(x);
+    return x;
+}
+// Sum over the lanes that share lane % S (S a power of two, 4 to 64): every
+// lane receives the sum over lanes l, l + S, l + 2S, ... of the wave.
+template <int S>
+__device__ __forceinline__ float sum_stride(float x) {
+    if constexpr (S <= 4) x += dpp_f32<0x124>(x);            // row_ror 4
+    if constexpr (S <= 8) x += dpp_f32<0x128>(x);            // row_ror 8
+    if constexpr (S <= 16) x = sum_xor16(x);
+    if constexpr (S <= 32) x = sum_xor32(x);
+    return x;
+}
+
 // Order-preserving key of a score for top-k selection: larger score -> larger
 // key; NaN below everything (key 0); -0 == +0.
 __device__ __forceinline__ uint32_t order_key(float x) {
@@ -79,15 +129,30 @@ __device__ __forceinline__ uint32_t key_prefix(uint32_t kmin, uint32_t kmax, int
     return top < 0 ? kmax : (kmin & ~((2u << top) - 1u));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+// Minimum / maximum of x over the wave, on the VALU (the pairing of max_lanes).
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off));
-    return x;
+    x = min(x, dpp_u32<0xB1>(x));
+    x = min(x, dpp_u32<0x4E>(x));
+    x = min(x, dpp_u32<0x141>(x));
+    x = min(x, dpp_u32<0x140>(x));
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = min(r[0], r[1]);
+    r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return min(r[0], r[1]);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
-    return x;
+    x = max(x, dpp_u32<0xB1>(x));
+    x = max(x, dpp_u32<0x4E>(x));
+    x = max(x, dpp_u32<0x141>(x));
+    x = max(x, dpp_u32<0x140>(x));
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max(r[0], r[1]);
+    r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max(r[0], r[1]);
 }
 
 // Number of set bits of `m` below this lane.
