@@ -80,6 +80,8 @@ CASES = [
                  v_sigma=0.0, sink_logit=16.0), [1e-3], "stem"),
     (wl.Workload("bl-bf16-sink-paged16-nb10", 1, 128 * 10, 2, 2, 128, 128, "bf16", sink=False,
                  sink_logit=16.0, paged=True, page_size=16), [1e-3, 1e-2], "dense"),
+    (wl.Workload("bl-fp8-gqa3-hq12-b2-paged32", 2, 128 * 10, 12, 4, 128, 128, "fp8", density=0.5,
+                 paged=True, page_size=32), [0.1], "stem"),
 ]
 
 

@@ -60,6 +60,11 @@ CASES = [
          keep="fixed:1000"),
     Case(wl.Workload("dec-bf16-keep-zero", 1, 128 * 8, 2, 1, 128, 128, "bf16"), [128 * 8 - 1], keep="fixed:0"),
     Case(wl.Workload("dec-bf16-len-clamped", 2, 128 * 4, 2, 1, 128, 128, "bf16"), [0, 10 ** 6]),
+    # a GQA group of 3 with batch 3 and 32-token pages; a group of 80 query
+    # heads, more than the scoring kernel stages at a time
+    Case(wl.Workload("dec-fp8-gqa3-hq12-b3-paged32", 3, 128 * 10, 12, 4, 128, 128, "fp8", paged=True,
+                     page_size=32), [128 * 10, 128 * 6 + 5, 77]),
+    Case(wl.Workload("dec-bf16-g80-d64-b64", 1, 64 * 16, 80, 1, 64, 64, "bf16"), [64 * 16 - 9]),
 ]
 
 

@@ -64,6 +64,8 @@ CASES = [
          [128 * 16, 128 * 11 + 90], [1e-3, 1e-2], keep="none"),
     Case(wl.Workload("dbl-fp8-sink-tpd", 1, 128 * 20, 8, 2, 128, 128, "fp8", sink=False, sink_logit=12.0),
          [128 * 20 - 1], [1e-3]),
+    Case(wl.Workload("dbl-fp8-gqa3-hq12-paged32", 2, 128 * 12, 12, 4, 128, 128, "fp8", paged=True, page_size=32),
+         [128 * 12, 128 * 8 + 3], [0.1]),
 ]
 
 

@@ -57,6 +57,12 @@ SMALL = [
     wl.Workload("bf16-paged16-d128-b128", 2, 128 * 19, 4, 2, 128, 128, "bf16", paged=True, page_size=16),
     wl.Workload("bf16-paged128-d128-b128", 1, 128 * 23, 8, 1, 128, 128, "bf16", paged=True, page_size=128,
                 density=0.5),
+    # GQA group of 3, head counts that are not a multiple of 8 (the plain head
+    # order on the XCDs), batch 3, 32-token pages, a single head
+    wl.Workload("fp8-gqa3-hq12-b3-paged32", 3, 128 * 11, 12, 4, 128, 128, "fp8", paged=True, page_size=32),
+    wl.Workload("bf16-gqa3-hq6-b3", 3, 128 * 9, 6, 2, 128, 128, "bf16", density=0.35),
+    wl.Workload("fp8-gqa3-hq24-b64-d64", 1, 64 * 21, 24, 8, 64, 64, "fp8", density=0.3),
+    wl.Workload("bf16-mha1", 1, 128 * 15, 1, 1, 128, 128, "bf16"),
 ]
 
 
