@@ -75,6 +75,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
             for (int c = 0; c < MAXC; ++c)
                 if (c < nch) cnt += __popcll(ballot64(key[c] >= cand));
             if (cnt >= want) t = cand;
+            // Exactly `want` keys are >= cand: they are the kept set whatever
+            // the lower bits hold, and with t = cand the rule below keeps
+            // every key > t and every key == t, i.e. exactly them.
+            if (cnt == want) break;
         }
         int gt = 0;
 #pragma unroll

@@ -180,6 +180,16 @@ def test_host_tpd_budget_equals_oracle_large(nb, dens):
     assert sb.stem_tpd_budget(nb, dens, 0.5) == oracle.tpd_budget(nb, dens, 0.5)
 
 
+def test_tpd_budget_repeated_and_interleaved_calls():
+    """The host keeps recent plans: more distinct (num_blocks, density, alpha)
+    than it keeps, called twice in interleaved order, each equal to the oracle."""
+    combos = [(nb, dens, alpha) for nb in (33, 70, 200) for dens in (0.1, 0.4) for alpha in (0.0, 0.5)]
+    want = {c: oracle.tpd_budget(*c) for c in combos}
+    for _ in range(2):
+        for c in combos + combos[::-1]:
+            assert sb.stem_tpd_budget(*c) == want[c], c
+
+
 def test_tpd_budget_errors():
     with pytest.raises(sb.StemError):
         sb.stem_tpd_budget(0, 0.5)
