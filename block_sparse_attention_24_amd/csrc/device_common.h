@@ -17,6 +17,13 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// 16 bytes read once (a streaming pass): a non-temporal load, which keeps the
+// stream from displacing reused data in the caches.
+__device__ __forceinline__ uint4 load16_stream(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // The 16 bytes of a load, widened to fp32.  ES = element size in bytes.
 // FP8 uses the gfx950 hardware conversion of OCP E4M3.
 template <int ES>

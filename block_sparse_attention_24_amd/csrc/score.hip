@@ -130,10 +130,10 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
     if (active) {
         const int rows = a.blk / kRowGroups;
         const int tok0 = blk_j * a.blk + group * rows;
-#pragma unroll 8
+#pragma unroll 16
         for (int t = 0; t < rows; ++t) {
             const size_t row = token_row(a.table, a.page_log2, a.pages_per_seq, a.seq, b, tok0 + t);
-            const uint4 u = *reinterpret_cast<const uint4 *>(a.base + row * row_bytes + (size_t)chunk * 16);
+            const uint4 u = load16_stream(a.base + row * row_bytes + (size_t)chunk * 16);
             float x[EPC];
             widen16<ES>(u, x);
             pool_add<EPC, MODE>(acc, x);
@@ -206,10 +206,10 @@ __device__ __forceinline__ void cache_write_body(const CacheArgs &a, int b, floa
                 float x[EPC];
 #pragma unroll
                 for (int i = 0; i < IN_VEC; ++i)
-                    widen16<ES_IN>(reinterpret_cast<const uint4 *>(in)[i], x + i * (16 / ES_IN));
+                    widen16<ES_IN>(load16_stream(in + 16 * i), x + i * (16 / ES_IN));
                 stored = quantize16_e4m3(x, scale);
             } else {
-                stored = *reinterpret_cast<const uint4 *>(in);   // same type: a copy
+                stored = load16_stream(in);                       // same type: a copy
             }
             const size_t row = token_row(a.table, a.page_log2, a.pages_per_seq, a.seq, b, tok);
             *reinterpret_cast<uint4 *>(dst + row * out_row_bytes + (size_t)chunk * 16) = stored;
