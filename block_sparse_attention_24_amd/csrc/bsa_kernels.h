@@ -1134,7 +1134,6 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         kb = kop(KRD, 1, 1);
         float ls[4];
         auto expq = [&](int t, int e0) {                  // P of 4 scores, into the partial sums
-            if (!soft) return;
 #pragma unroll
             for (int e = e0; e < e0 + 4; ++e) {
                 const float pe = __builtin_amdgcn_exp2f(fmaf(sc[t][e], c, -mc));
@@ -1143,50 +1142,48 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             }
         };
         auto packq = [&](int w) {                          // 4 P of P word w as E4M3
-            if (!soft) return;
             const f32x16 &src = sc[w >> 2];
             const int ee = 4 * (w & 3);
             // the word's old contents (P of block j-2, consumed) are the tied operand
             const int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], pv_out[w], false);
             pv_out[w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
         };
-        expq(0, 0);
+        // one softmax slice per MFMA slot, skipped as a whole (one wave-uniform
+        // branch) when no row of the wave keeps block j
+        auto slice = [&](auto f) {
+            if (soft) f();
+        };
+        slice([&] { expq(0, 0); });
         SB();
         sn[0] = mfma8(ka, qop(1), sn[0], 127);
         SB();
         dma_v(integral_constant<int, 0>{});
         i32x8 vb = vop(VRD, 1);
-        expq(0, 4);
-        packq(0);
+        slice([&] { expq(0, 4); packq(0); });
         SB();
         sn[1] = mfma8(kb, qop(1), sn[1], 127);
         SB();
         kfirst = kop(KST + ((R + 2) % NST) * TILE, 0, 0);  // K(j+2): the first operand of S(j+2)
         dma_v(integral_constant<int, 1>{});
-        expq(0, 8);
-        packq(1);
+        slice([&] { expq(0, 8); packq(1); });
         SB();
         o[0] = mfma8(va, pv_in, o[0], psc_in);
         SB();
         va = vop(VRD, 2);
-        expq(0, 12);
-        packq(2);
-        packq(3);
+        slice([&] { expq(0, 12); packq(2); packq(3); });
         SB();
         o[1] = mfma8(vb, pv_in, o[1], psc_in);
         SB();
         vb = vop(VRD, 3);
-        expq(1, 0);
+        slice([&] { expq(1, 0); });
         SB();
         o[2] = mfma8(va, pv_in, o[2], psc_in);
         SB();
-        expq(1, 4);
-        packq(4);
+        slice([&] { expq(1, 4); packq(4); });
         SB();
         o[3] = mfma8(vb, pv_in, o[3], psc_in);
         SB();
-        expq(1, 8);
-        packq(5);
+        slice([&] { expq(1, 8); packq(5); });
         if constexpr (SKIP) {
             // made here, each block, so that it holds no registers through the region
 #pragma unroll
@@ -1195,9 +1192,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         SB();
         lacc = mfma8(ones, pv_in, lacc, psc_in);
         SB();
-        expq(1, 12);
-        packq(6);
-        packq(7);
+        slice([&] { expq(1, 12); packq(6); packq(7); });
         if (soft) {
             const int ice = (int)ce;
             l = fmaf(l, alpha, ldexpf((ls[0] + ls[1]) + (ls[2] + ls[3]), ice - 8));
