@@ -305,10 +305,23 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     if (I0 >= a.nb || J0 >= a.nb) return;      // nothing of this quarter is stored
 
     if (J0 > I0 + 63) {               // this quarter lies wholly above the diagonal
-        for (int i = 0; i < 64; ++i) {
-            const int I = I0 + i;
-            if (I >= a.nb) break;
-            if (J0 + lane < a.nb) out[(size_t)I * a.nb + J0 + lane] = ninf;
+        if ((a.nb & 3) == 0) {
+            // rows start 16-byte aligned: four rows of 64 columns per store
+            // instruction, 16 bytes per lane
+            const int c4 = J0 + 4 * (lane & 15);
+            if (c4 < a.nb) {
+                for (int i = lane >> 4; i < 64; i += 4) {
+                    const int I = I0 + i;
+                    if (I >= a.nb) break;
+                    *reinterpret_cast<f32x4 *>(out + (size_t)I * a.nb + c4) = f32x4{ninf, ninf, ninf, ninf};
+                }
+            }
+        } else {
+            for (int i = 0; i < 64; ++i) {
+                const int I = I0 + i;
+                if (I >= a.nb) break;
+                if (J0 + lane < a.nb) out[(size_t)I * a.nb + J0 + lane] = ninf;
+            }
         }
         return;
     }
