@@ -190,6 +190,20 @@ def test_tpd_budget_repeated_and_interleaved_calls():
             assert sb.stem_tpd_budget(*c) == want[c], c
 
 
+def test_tpd_budget_concurrent_callers():
+    """Threads calling with different parameters at once (ctypes releases the
+    GIL during the call, so the library's plan cache is shared for real):
+    every result equals the oracle's."""
+    import concurrent.futures as cf
+    combos = [(nb, dens, alpha) for nb in (150, 301, 512) for dens in (0.07, 0.3, 0.6) for alpha in (0.0, 0.5, 1.0)]
+    want = {c: oracle.tpd_budget(*c) for c in combos}
+    jobs = combos * 4
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        got = list(ex.map(lambda c: sb.stem_tpd_budget(*c), jobs))
+    for c, g in zip(jobs, got):
+        assert g == want[c], c
+
+
 def test_tpd_budget_errors():
     with pytest.raises(sb.StemError):
         sb.stem_tpd_budget(0, 0.5)
