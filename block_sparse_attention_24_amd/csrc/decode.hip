@@ -256,12 +256,17 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
     const int g = bg % a.hkv, b = bg / a.hkv;
     const int h = g * G + hh;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int slot = s * kSplit + wave;             // this wave's place in the list it walks
+    const size_t row_list = ((size_t)b * a.hq + h) * a.nb;
+    // The entry of the list this wave walks is read before the count is known,
+    // at an index clamped into the row (a value past the count is never
+    // used), so that the two loads overlap instead of following each other.
+    const int first = MODE == kPV ? a.live[row_list + min(slot, a.nb - 1)] : a.lists[row_list + min(slot, a.nb - 1)];
     // the PV pass walks the entries that were not dropped
     const int count = MODE == kPV ? a.nlive[(size_t)b * a.hq + h] : a.counts[(size_t)b * a.hq + h];
     if (s * kSplit >= count) return;                // the whole workgroup exits together
     const int t = seq_len_of(a, b) - 1;
-    const int slot = s * kSplit + wave;             // this wave's place in the list it walks
-    const int e = MODE == kPV ? (slot < count ? a.live[((size_t)b * a.hq + h) * a.nb + slot] : 0) : slot;
+    const int e = MODE == kPV ? (slot < count ? first : 0) : slot;
     const int r = lane / CPR, c = lane % CPR;       // row within a pass, chunk within the row
     const size_t row_bytes = (size_t)a.hkv * D * ES;
     const size_t col = (size_t)g * D * ES + (size_t)c * 16;
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
     const bool live = slot < count;
 
     if (live) {
-        const int J = a.lists[((size_t)b * a.hq + h) * a.nb + e];
+        const int J = MODE == kPV ? a.lists[row_list + e] : first;
         const int tok0 = J * BLK;
         const int nkeys = min(BLK, t - tok0 + 1);
         // this lane's slice of q, scaled so that q.k is in log2 units
