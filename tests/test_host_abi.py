@@ -4,6 +4,7 @@ enqueued, and the host TPD budget equals the oracle's.  No GPU is used: the
 calls below either never reach HIP (invalid arguments) or are host-only
 (stem_tpd_budget)."""
 
+import math
 import ctypes
 import os
 import re
@@ -202,6 +203,46 @@ def test_tpd_budget_concurrent_callers():
         got = list(ex.map(lambda c: sb.stem_tpd_budget(*c), jobs))
     for c, g in zip(jobs, got):
         assert g == want[c], c
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0])
+def test_tpd_budget_max_blocks_properties(alpha):
+    """At the largest block count the API takes (65,536) the oracle's
+    one-grant-at-a-time simulation is too slow, so the budget is pinned by the
+    properties that define water-filling: the total, the forced rows, the
+    bounds, and that no grant was given out of order.  The last grant a row
+    received, (I, k_I), comes no later than the next grant any row with room
+    could take, (I', k_I' + 1), in the order of key (n / (I+1)^(1-alpha),
+    compared exactly in integers) and then row."""
+    nb, dens = 65536, 0.25
+    k, total = sb.stem_tpd_budget(nb, dens, alpha)
+    c = nb * (nb + 1) // 2
+    assert total == max(2 * nb - 1, min(c, math.floor(dens * c + 0.5)))
+    assert sum(k) == total
+    assert k[0] == 1 and all(2 <= k[i] <= i + 1 for i in range(1, nb))
+    p = {0.0: 1, 0.5: 2, 1.0: 0}[alpha]      # key n^p / (I+1), or n alone for alpha = 1
+
+    def key(row, n):                          # (numerator, denominator) of the key, and the row
+        return (n, 1, row) if p == 0 else (n ** p, row + 1, row)
+
+    def before(a, b):                         # grant a strictly before grant b
+        l, r = a[0] * b[1], b[0] * a[1]
+        return l < r or (l == r and a[2] < b[2])
+
+    last = None                               # the latest grant given
+    for i in range(1, nb):
+        if k[i] > 2:
+            g = key(i, k[i])
+            if last is None or before(last, g):
+                last = g
+    nxt = None                                # the earliest grant still open
+    for i in range(1, nb):
+        if k[i] < i + 1:
+            g = key(i, k[i] + 1)
+            if nxt is None or before(g, nxt):
+                nxt = g
+    assert last is not None and nxt is not None
+    assert before(last, nxt)
 
 
 def test_tpd_budget_errors():
