@@ -288,6 +288,28 @@ def test_selection_special_values():
         assert np.array_equal(mask_bits(mask, nb), want), (density, alpha)
 
 
+@pytest.mark.parametrize("nb,density,alpha", [(4096, 0.03, 0.5), (3000, 0.02, 0.0)])
+def test_selection_many_blocks(nb, density, alpha):
+    """More than 2048 key blocks per row, so each lane holds up to 64 keys
+    (the widest selection instantiation); scores rounded to two decimals, so
+    ties are common.  Mask, counts and sampled kept lists against the oracle's
+    rule.  (Low densities keep the oracle's grant-by-grant budget fast.)"""
+    _announce(f"selection nb={nb} density={density} alpha={alpha}")
+    p = sb.Problem(1, 64 * nb, 1, 1, 64, 64, "bf16")
+    rng = np.random.default_rng(nb)
+    s = np.round(rng.standard_normal((1, 1, nb, nb)), 2).astype(np.float32)
+    scores = torch.from_numpy(s).to(DEV)
+    mask, lst, cnt = sb.select(p, scores, density, alpha, with_list=True)
+    torch.cuda.synchronize()
+    budget, _ = oracle.tpd_budget(nb, density, alpha)
+    want = oracle.select_blocks(s.astype(np.float64), budget)
+    assert np.array_equal(mask_bits(mask, nb), want)
+    assert np.array_equal(cnt.cpu().numpy()[0, 0], np.asarray(budget))
+    lists = lst.cpu().numpy()[0, 0]
+    for i in list(range(0, nb, 97)) + [nb - 1]:
+        assert list(lists[i, :budget[i]]) == list(np.nonzero(want[0, 0, i])[0]), i
+
+
 def test_zero_value_block():
     w = wl.Workload("zero-v-block", 1, 128 * 16, 2, 1, 128, 128, "bf16")
     _announce(w.name)
