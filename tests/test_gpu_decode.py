@@ -65,6 +65,11 @@ CASES = [
     Case(wl.Workload("dec-fp8-gqa3-hq12-b3-paged32", 3, 128 * 10, 12, 4, 128, 128, "fp8", paged=True,
                      page_size=32), [128 * 10, 128 * 6 + 5, 77]),
     Case(wl.Workload("dec-bf16-g80-d64-b64", 1, 64 * 16, 80, 1, 64, 64, "bf16"), [64 * 16 - 9]),
+    # 1,500 and 3,000 key blocks: the 32- and 64-chunk selection instantiations
+    Case(wl.Workload("dec-bf16-nb1500-d64-b64", 1, 64 * 1500, 2, 1, 64, 64, "bf16"), [64 * 1500 - 3],
+         keep="fixed:150"),
+    Case(wl.Workload("dec-fp8-nb3000-d64-b64-paged16", 2, 64 * 3000, 2, 1, 64, 64, "fp8", paged=True,
+                     page_size=16), [64 * 3000, 64 * 2222 + 9], keep="fixed:300"),
 ]
 
 
