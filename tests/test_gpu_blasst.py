@@ -82,6 +82,11 @@ CASES = [
                  sink_logit=16.0, paged=True, page_size=16), [1e-3, 1e-2], "dense"),
     (wl.Workload("bl-fp8-gqa3-hq12-b2-paged32", 2, 128 * 10, 12, 4, 128, 128, "fp8", density=0.5,
                  paged=True, page_size=32), [0.1], "stem"),
+    # the remaining (dtype, mask, layout) instantiations: fp8 dense paged, bf16 sparse paged
+    (wl.Workload("bl-fp8-dense-paged32-nb9", 1, 128 * 9, 4, 2, 128, 128, "fp8", sink=False, v_sigma=0.0,
+                 paged=True, page_size=32), [0.05, 0.8], "dense"),
+    (wl.Workload("bl-bf16-stem-paged64-b2-nb11", 2, 128 * 11, 4, 2, 128, 128, "bf16", density=0.5,
+                 paged=True, page_size=64), [0.02, 0.3], "stem"),
 ]
 
 
