@@ -65,6 +65,17 @@ CASES = [
     Case(wl.Workload("dec-fp8-gqa3-hq12-b3-paged32", 3, 128 * 10, 12, 4, 128, 128, "fp8", paged=True,
                      page_size=32), [128 * 10, 128 * 6 + 5, 77]),
     Case(wl.Workload("dec-bf16-g80-d64-b64", 1, 64 * 16, 80, 1, 64, 64, "bf16"), [64 * 16 - 9]),
+    # the remaining (dtype, head_dim, block) instantiations of the decode kernels
+    Case(wl.Workload("dec-fp8-d128-b64", 1, 64 * 20, 4, 2, 128, 64, "fp8"), [64 * 20 - 1]),
+    Case(wl.Workload("dec-fp8-d64-b128-paged32", 1, 128 * 9, 2, 1, 64, 128, "fp8", paged=True, page_size=32),
+         [128 * 9 - 40]),
+    Case(wl.Workload("dec-bf16-d128-b64-paged16", 2, 64 * 18, 4, 1, 128, 64, "bf16", paged=True, page_size=16),
+         [64 * 18, 64 * 7 + 3]),
+    Case(wl.Workload("dec-bf16-d64-b128", 1, 128 * 10, 2, 2, 64, 128, "bf16"), [128 * 10 - 2]),
+    Case(wl.Workload("dec-f32-d64-b64", 1, 64 * 15, 2, 1, 64, 64, "f32"), [64 * 15 - 1]),
+    Case(wl.Workload("dec-f32-d64-b128-paged64", 1, 128 * 8, 2, 1, 64, 128, "f32", paged=True, page_size=64),
+         [128 * 8 - 17]),
+    Case(wl.Workload("dec-f32-d128-b128", 1, 128 * 8, 2, 1, 128, 128, "f32"), [128 * 8 - 5]),
     # 1,500 and 3,000 key blocks: the 32- and 64-chunk selection instantiations
     Case(wl.Workload("dec-bf16-nb1500-d64-b64", 1, 64 * 1500, 2, 1, 64, 64, "bf16"), [64 * 1500 - 3],
          keep="fixed:150"),
