@@ -66,6 +66,17 @@ CASES = [
          [128 * 20 - 1], [1e-3]),
     Case(wl.Workload("dbl-fp8-gqa3-hq12-paged32", 2, 128 * 12, 12, 4, 128, 128, "fp8", paged=True, page_size=32),
          [128 * 12, 128 * 8 + 3], [0.1]),
+    # the remaining (dtype, head_dim, block) instantiations of the two passes
+    Case(wl.Workload("dbl-fp8-d128-b64", 1, 64 * 20, 4, 2, 128, 64, "fp8"), [64 * 20 - 1], [0.2]),
+    Case(wl.Workload("dbl-fp8-d64-b64-paged16", 1, 64 * 16, 2, 1, 64, 64, "fp8", paged=True, page_size=16),
+         [64 * 16 - 7], [0.2]),
+    Case(wl.Workload("dbl-fp8-d64-b128", 1, 128 * 9, 2, 1, 64, 128, "fp8"), [128 * 9 - 40], [0.2]),
+    Case(wl.Workload("dbl-bf16-d128-b64-paged32", 1, 64 * 18, 4, 1, 128, 64, "bf16", paged=True, page_size=32),
+         [64 * 18 - 2], [0.2]),
+    Case(wl.Workload("dbl-bf16-d64-b128", 1, 128 * 10, 2, 2, 64, 128, "bf16"), [128 * 10 - 2], [0.2]),
+    Case(wl.Workload("dbl-f32-d64-b64", 1, 64 * 15, 2, 1, 64, 64, "f32"), [64 * 15 - 1], [0.2]),
+    Case(wl.Workload("dbl-f32-d64-b128", 1, 128 * 8, 2, 1, 64, 128, "f32"), [128 * 8 - 17], [0.2]),
+    Case(wl.Workload("dbl-f32-d128-b128", 1, 128 * 8, 2, 1, 128, 128, "f32"), [128 * 8 - 5], [0.2]),
 ]
 
 
