@@ -307,6 +307,28 @@ __device__ __forceinline__ void pack_p(PPack<DT, D, BLK> &pk, const f32x16 (&p)[
     }
 }
 
+// FP8: the residual P - E4M3(P) of every packed P, itself rounded to E4M3 (the
+// difference is exact in fp32: P and its E4M3 value lie within a factor of
+// two).  PV with both terms carries about seven significant bits of P.
+template <int DT, int D, int BLK>
+__device__ __forceinline__ void pack_residual(PPack<DT, D, BLK> &lo, const PPack<DT, D, BLK> &hi,
+                                              const f32x16 (&p)[Geo<DT, D, BLK>::NTW]) {
+    using G = Geo<DT, D, BLK>;
+    static_assert(DT == kFP8, "FP8 only");
+#pragma unroll
+    for (int t = 0; t < G::NTW; t += 2)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const int e = 4 * w;
+            const f32x16 &src = p[t + (e >> 4)];
+            const int ee = e & 15;
+            const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi.f8[t >> 1][w], false);
+            const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi.f8[t >> 1][w], true);
+            const int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee] - h01[0], src[ee + 1] - h01[1], 0, false);
+            lo.f8[t >> 1][w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2] - h23[0], src[ee + 3] - h23[1], x, true);
+        }
+}
+
 // O^T[dt] += V^T P^T over this wave's keys of the block (tiles t0 .. t0+NTW-1).
 // For FP8 the softmax denominator is accumulated by the MFMA as well (an
 // all-ones row of V^T), so that it sums exactly the quantised P that
@@ -578,6 +600,10 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
     f32x16 s[G::NTW];                                     // scores of the block awaiting softmax
     PPack<DT, D, BLK> pk = {};                            // P of the block awaiting PV (zero before the first)
     int pscale = 127;                                     // its E8M0 scale (FP8)
+    // FP8: the row's first kept block (the forced sink block of a Stem mask,
+    // where attention mass concentrates) also multiplies V by the residual of
+    // its P, so that its P carries about seven significant bits.
+    PPack<DT, D, BLK> plo = {};
     const int nph = 2 * n + 2;
 
     auto phase = [&](auto R, int p) {
@@ -608,6 +634,9 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
                         for (int t = 0; t < G::NTW; ++t) s[t] = qk_tile<DT, D, BLK>(qf, kl, t0 + t, lane);
                     }
                     if (j >= 1) pv_block<DT, D, BLK>(o, lacc, pk, vl, t0, lane, pscale);
+                }
+                if constexpr (DT == kFP8) {
+                    if (j == 1) pv_block<DT, D, BLK>(o, lacc, plo, vl, t0, lane, pscale);   // residual of P(0)
                 }
             } else if (j < n) {
                 // ---- VALU phase: online softmax of block j
@@ -671,6 +700,9 @@ __global__ __launch_bounds__((Geo<DT, D, BLK>::NT), 1) void bsa_kernel(BsaArgs a
                 const float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
                 l += DT == kFP8 ? ldexpf(ls, -e) : ls;
                 pack_p<DT, D, BLK>(pk, s);
+                if constexpr (DT == kFP8) {
+                    if (j == 0) pack_residual<DT, D, BLK>(plo, pk, s);
+                }
                 pscale = 127 - e;
             }
         }
@@ -771,12 +803,13 @@ constexpr int NST = 4;                           // LDS stages of K and of V
 constexpr int TILE = BLK * D;                    // bytes of one K or V block
 constexpr int KST = 0, VST = NST * TILE;         // K stages, then V stages
 constexpr int LIST_OFF = 2 * NST * TILE;         // kept-block list (u16) after the stages
-constexpr int LIST = 4096;
+constexpr int LIST = 4096 + 8;                   // up to 4096 kept blocks, plus 8 pad entries
 constexpr int WSUM_OFF = LIST_OFF + 2 * LIST;    // per-wave counts of the list scan
 constexpr int ML_OFF = WSUM_OFF + 4 * NW;        // (M, l, lq) of the second key half
 constexpr int HM_OFF = ML_OFF + 3 * 4 * 64 * 4;  // online skip: half-block maxima, [parity][wave][lane]
 constexpr int SMEM = HM_OFF;
 constexpr int SMEM_SKIP = HM_OFF + 2 * NW * 64 * 4;
+static_assert(SMEM_SKIP <= 160 * 1024, "LDS of one CU");
 constexpr int VM_ITER = 4;                       // loads into LDS per wave and iteration
 constexpr float THRESH = 8.0f;                   // lazy rescale: P stays below 2^THRESH
 constexpr float M_NONE = -3.0e38f;               // running max before any finite score
@@ -814,12 +847,14 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void *p) {
 // into LDS at byte lds + OFF + 16 * lane.  Written as asm so that the compiler,
 // which would otherwise make every later transposing LDS read wait for all such
 // loads, leaves the pacing to the explicit vmcnt waits.  The asm has no
-// outputs; m0 is used by nothing else in these kernels.
+// outputs; m0 is used by nothing else in these kernels.  s_add_u32 writes
+// the scalar condition code (its carry), so SCC is declared clobbered: a
+// comparison the compiler placed before the asm must not be branched on after it.
 template <int OFF>
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned lds, unsigned voff, unsigned soff) {
     asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
-                    "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(OFF) : "memory", "m0");
+                    "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(OFF) : "memory", "m0", "scc");
 }
 }  // namespace fp8p
 
@@ -960,9 +995,10 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     const int jdiag = list_at(last) == I ? last : -1;     // the diagonal block, if kept, is the last
 
     // ---- prologue --------------------------------------------------------------
-    // As if iterations -3 .. -1 had run: K(0..3) and V(0..1) loading, V(-1)
-    // standing in V stage 3 (a copy of V(0): the first PV multiplies it by
-    // P = 0, so it only has to be finite, which V(0) is wherever O is).
+    // As if iterations -3 .. -1 had run: K(0..3) and V(0..1) loading, and V
+    // stage 3 loaded with a copy of V(0) that no iteration reads (iteration 0
+    // has no PV of a previous block); it keeps the count of loads in flight
+    // the same at every iteration's wait.
     {
         const unsigned s0 = src_off(list_at(0));
         const unsigned s1 = src_off(list_at(min(1, last)));
@@ -1048,8 +1084,18 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     f32x16 sB[2];
     i32x8 pkB = {};
     int pscB = 127;
-    auto iter = [&](auto RR, int j) {
+    // The row's first kept block carries a second E4M3 term: the residual
+    // P - E4M3(P) at the same scale, so that its P reaches O with about seven
+    // significant bits instead of four.  The first block is the forced sink
+    // block of a Stem mask, where attention mass concentrates.  Iteration 0
+    // has no previous block to multiply, so its PV slots are free: at its
+    // barrier V(0) has already landed, O and the MFMA row sums are still zero
+    // (so block 0 needs no rescale), and the residual's PV is added at the end
+    // of the iteration at block 0's scale.  The MFMA count per row is unchanged.
+    // PH: 0 any iteration; 1 iteration 0.
+    auto iter = [&](auto RR, auto PHC, int j) {
         constexpr int R = decltype(RR)::value;
+        constexpr int PH = decltype(PHC)::value;
         constexpr int KRD = KST + ((R + 1) % NST) * TILE, VRD = ((R + 3) % NST) * TILE;
         f32x16(&sc)[2] = (R & 1) ? sB : s;                 // scores of block j
         f32x16(&sn)[2] = (R & 1) ? s : sB;                 // scores of block j+1
@@ -1081,7 +1127,8 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         auto dma_v = [&](auto I) { load_lds16<VDM + 8 * decltype(I)::value * D>(vrs, lds_wave, (unsigned)dv[I], so_v); };
 #define SB() __builtin_amdgcn_sched_barrier(0)
         i32x8 ka = kfirst, kb = kop(KRD, 1, 0);
-        i32x8 va = vop(VRD, 0);
+        i32x8 va = PH == 1 ? i32x8{} : vop(VRD, 0);
+        i32x8 plo = {};                                    // PH == 1: residual of P(0)
         // the decision, after the first operand reads so that their latency and
         // the other half's maximum overlap; soft: some row of the wave keeps
         // block j (always, without the skip); the softmax slices are branched
@@ -1147,6 +1194,14 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             // the word's old contents (P of block j-2, consumed) are the tied operand
             const int x = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee], src[ee + 1], pv_out[w], false);
             pv_out[w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2], src[ee + 3], x, true);
+            if constexpr (PH == 1) {
+                // residual of P(0): exact in fp32 (P and its E4M3 value lie within
+                // a factor of two), then rounded to E4M3 itself
+                const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(pv_out[w], false);
+                const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(pv_out[w], true);
+                const int y = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee] - h01[0], src[ee + 1] - h01[1], plo[w], false);
+                plo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2] - h23[0], src[ee + 3] - h23[1], y, true);
+            }
         };
         // one softmax slice per MFMA slot, skipped as a whole (one wave-uniform
         // branch) when no row of the wave keeps block j
@@ -1158,7 +1213,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         sn[0] = mfma8(ka, qop(1), sn[0], 127);
         SB();
         dma_v(integral_constant<int, 0>{});
-        i32x8 vb = vop(VRD, 1);
+        i32x8 vb = PH == 1 ? i32x8{} : vop(VRD, 1);
         slice([&] { expq(0, 4); packq(0); });
         SB();
         sn[1] = mfma8(kb, qop(1), sn[1], 127);
@@ -1166,22 +1221,26 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         kfirst = kop(KST + ((R + 2) % NST) * TILE, 0, 0);  // K(j+2): the first operand of S(j+2)
         dma_v(integral_constant<int, 1>{});
         slice([&] { expq(0, 8); packq(1); });
+        // PV(j-1) (none in iteration 0)
+        auto pv = [&](int dt, const i32x8 &vx) {
+            if constexpr (PH != 1) o[dt] = mfma8(vx, pv_in, o[dt], psc_in);
+        };
         SB();
-        o[0] = mfma8(va, pv_in, o[0], psc_in);
+        pv(0, va);
         SB();
-        va = vop(VRD, 2);
+        if constexpr (PH != 1) va = vop(VRD, 2);
         slice([&] { expq(0, 12); packq(2); packq(3); });
         SB();
-        o[1] = mfma8(vb, pv_in, o[1], psc_in);
+        pv(1, vb);
         SB();
-        vb = vop(VRD, 3);
+        if constexpr (PH != 1) vb = vop(VRD, 3);
         slice([&] { expq(1, 0); });
         SB();
-        o[2] = mfma8(va, pv_in, o[2], psc_in);
+        pv(2, va);
         SB();
         slice([&] { expq(1, 4); packq(4); });
         SB();
-        o[3] = mfma8(vb, pv_in, o[3], psc_in);
+        pv(3, vb);
         SB();
         slice([&] { expq(1, 8); packq(5); });
         if constexpr (SKIP) {
@@ -1190,7 +1249,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             for (int w = 0; w < 8; ++w) asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(ones[w]));
         }
         SB();
-        lacc = mfma8(ones, pv_in, lacc, psc_in);
+        if constexpr (PH != 1) lacc = mfma8(ones, pv_in, lacc, psc_in);
         SB();
         slice([&] { expq(1, 12); packq(6); packq(7); });
         if (soft) {
@@ -1203,6 +1262,14 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             alpha = 1.0f;                                  // M, l unchanged
         }
         SB();
+        if constexpr (PH == 1) {
+            // O and lacc are zero: no rescale is due, and the residual of P(0)
+            // multiplies V(0) (V stage 0) at block 0's scale
+            alpha = 1.0f;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma8(vop(0, dt), plo, o[dt], psc_out);
+            lacc = mfma8(ones, plo, lacc, psc_out);
+        }
         if constexpr (SKIP) {
             // the next block's half max, for the decision at the next barrier
             if (j + 1 == jdiag) {
@@ -1223,11 +1290,13 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         lk = list_raw(j + 7);                              // iteration j+3
         lv = list_raw(j + 5);
     };
-    for (int j = 0; j < n; j += NST) {
-        iter(std::integral_constant<int, 0>{}, j);
-        if (j + 1 < n) iter(std::integral_constant<int, 1>{}, j + 1);
-        if (j + 2 < n) iter(std::integral_constant<int, 2>{}, j + 2);
-        if (j + 3 < n) iter(std::integral_constant<int, 3>{}, j + 3);
+    using PH0 = integral_constant<int, 0>;
+    iter(integral_constant<int, 0>{}, integral_constant<int, 1>{}, 0);
+    for (int j = 1; j < n; j += NST) {
+        iter(integral_constant<int, 1>{}, PH0{}, j);
+        if (j + 1 < n) iter(integral_constant<int, 2>{}, PH0{}, j + 1);
+        if (j + 2 < n) iter(integral_constant<int, 3>{}, PH0{}, j + 2);
+        if (j + 3 < n) iter(integral_constant<int, 0>{}, PH0{}, j + 3);
     }
     sync_vm<2 * VM_ITER>();                                // V(n-1) has landed
     rescale_o();
@@ -1308,7 +1377,7 @@ constexpr int ROWB = D * 2;                      // bytes of a K or V row
 constexpr int TILE = BLK * ROWB;                 // bytes of a K or V block
 constexpr int KST = 0, VST = 2 * TILE;           // two K stages, then two V stages
 constexpr int LIST_OFF = 4 * TILE;               // kept-block list (u16) after the stages
-constexpr int LIST = 4096;
+constexpr int LIST = 4096 + 8;                   // up to 4096 kept blocks, plus 8 pad entries
 constexpr int WSUM_OFF = LIST_OFF + 2 * LIST;    // per-wave counts of the list scan
 constexpr int ML_OFF = WSUM_OFF + 4 * NW;        // (M, l) of the second key half
 constexpr int HM_OFF = ML_OFF + 2 * 4 * 64 * 4;  // online skip: half-block maxima, [parity][wave][lane]

@@ -5,7 +5,14 @@ The fp8 attention kernel issues its loads into LDS from inline asm, which sets
 m0 (the LDS address of such loads) and declares it clobbered.  That is sound
 only while no compiler-generated code in the same object keeps anything in m0:
 every write of m0 there must be the asm's own `s_add_u32 m0, ...`, directly
-followed by its `buffer_load_dwordx4 ... lds`."""
+followed by its `buffer_load_dwordx4 ... lds`.
+
+That `s_add_u32` also writes the scalar condition code (SCC, its carry).  The
+asm declares SCC clobbered; without that, the compiler kept a comparison's
+result in SCC across the asm and branched on the carry instead (the causal
+mask of the diagonal block was then applied to the first block).  So after
+each such asm, no instruction may read SCC before code of the compiler's own
+has written it again."""
 
 from __future__ import annotations
 
@@ -56,3 +63,32 @@ def test_m0_written_only_by_the_lds_loads(obj):
         assert nxt.startswith("buffer_load_dwordx4") and nxt.endswith("offen lds"), (text, nxt)
         writes += 1
     assert writes > 0, "the loads into LDS were not found"
+
+
+# SALU instructions that write SCC, and the ones that read it
+_SCC_WRITE = re.compile(r"^s_(add_|sub_|addc_|subb_|and_|or_|xor_|andn2_|orn2_|nand_|nor_|xnor_|lshl|lshr_|ashr_|bfe_|"
+                        r"min_|max_|abs_|absdiff_|not_|bcnt|cmp|bitcmp|quadmask|wqm)")
+_SCC_READ = re.compile(r"^s_(cbranch_scc|cselect_|addc_|subb_|cmov)")
+
+
+@pytest.mark.parametrize("obj", OBJS, ids=os.path.basename)
+def test_no_branch_on_the_condition_code_the_lds_loads_write(obj):
+    if not os.path.exists(obj):
+        pytest.skip("attention object not built (python -m block_sparse_attention_24_amd.build)")
+    if not all(os.path.exists(os.path.join(LLVM, t)) for t in ("llvm-objcopy", "clang-offload-bundler",
+                                                                  "llvm-objdump")):
+        pytest.skip("LLVM tools not found")
+    ins = _disassemble(obj)
+    ours = re.compile(r"^s_add_u32 m0, s\d+, (0x[0-9a-f]+|\d+)$")
+    after_asm = False
+    bad = []
+    for i, text in enumerate(ins):
+        op = text.split()[0] if text else ""
+        if ours.match(text):
+            after_asm = True
+            continue
+        if _SCC_READ.match(op) and after_asm:
+            bad.append((i, text))
+        if _SCC_WRITE.match(op) or op.startswith("s_endpgm"):
+            after_asm = False
+    assert not bad, f"SCC read after an LDS load's s_add_u32 m0 with no write in between: {bad[:5]}"
