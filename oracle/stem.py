@@ -318,9 +318,8 @@ def _attend(qrows, pos, keys_idx, diag_kept, i_blk, block, k_h, v_h, tau):
     `keys_idx`; inside the diagonal block a key j is visible only if j <= i.
     A skipped key block contributes nothing, exactly as a -inf logit would
     (Stem-cn §二.2.2).  Rows with no visible key give O = 0, LSE = -inf."""
-    d = qrows.shape[-1]
     if keys_idx.size == 0:
-        return np.zeros((len(pos), d)), np.full(len(pos), -np.inf)
+        return np.zeros((len(pos), v_h.shape[-1])), np.full(len(pos), -np.inf)
     logits = tau * (qrows @ k_h[keys_idx].T)                     # [rows, keys]
     if diag_kept:
         diag_start = i_blk * block
@@ -335,9 +334,10 @@ def _attend(qrows, pos, keys_idx, diag_kept, i_blk, block, k_h, v_h, tau):
 
 
 def block_sparse_attention(q, k, v, block_mask, block, softmax_scale=None):
-    """O[b, S, Hq, d] and LSE[b, Hq, S] (natural log) of causal attention that
+    """O[b, S, Hq, dv] and LSE[b, Hq, S] (natural log) of causal attention that
     only sees the kept key blocks of each query block (block_mask [b,Hq,Nb,Nb]
-    bool)."""
+    bool).  V may be wider or narrower than Q and K (dv = v.shape[-1]): each
+    output column is the softmax-weighted mean of that column of V."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -346,7 +346,7 @@ def block_sparse_attention(q, k, v, block_mask, block, softmax_scale=None):
     group = Hq // Hkv
     nb = S // block
     tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    o = np.zeros((b, S, Hq, d))
+    o = np.zeros((b, S, Hq, v.shape[-1]))
     lse = np.full((b, Hq, S), -np.inf)
     for bi in range(b):
         for h in range(Hq):
@@ -365,13 +365,14 @@ def attention_rows(q, k, v, block_mask, block, rows, softmax_scale=None):
     """The same definition evaluated only at the (batch, head, token) triples
     in `rows`: for sampled checks at sizes where the full oracle is too slow.
     block_mask is None for dense causal attention, else a callable
-    (b, h, I) -> bool row of length Nb or an array [b, Hq, Nb, Nb]."""
+    (b, h, I) -> bool row of length Nb or an array [b, Hq, Nb, Nb].  O has V's
+    width."""
     S, Hq, d = q.shape[1], q.shape[2], q.shape[3]
     Hkv = k.shape[2]
     group = Hq // Hkv
     nb = S // block
     tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    out_o = np.zeros((len(rows), d))
+    out_o = np.zeros((len(rows), v.shape[-1]))
     out_l = np.zeros(len(rows))
     groups = {}                                   # rows of one query block share its keys
     for n, (bi, h, i) in enumerate(rows):
@@ -435,8 +436,7 @@ def _attend_blasst(qrows, pos, kept_blocks, i_blk, block, k_h, v_h, tau, lam):
         keys_all.append(keys)
         logits_all.append(np.where(drop[:, None], -np.inf, lg))
     if not keys_all:
-        d = qrows.shape[-1]
-        return np.zeros((rows, d)), np.full(rows, -np.inf), dropped, closest
+        return np.zeros((rows, v_h.shape[-1])), np.full(rows, -np.inf), dropped, closest
     keys_idx = np.concatenate(keys_all)
     logits = np.concatenate(logits_all, axis=1)
     top = logits.max(axis=1)
@@ -463,8 +463,8 @@ def blasst_attention(q, k, v, block_mask, block, lam, softmax_scale=None):
     """Block-sparse causal attention with the BLASST online skip (see
     _attend_blasst) inside every row's loop over its kept blocks.
     block_mask [b, Hq, Nb, Nb] bool, or None for every causal block (the
-    pages' setting: the skip inside dense attention).  Returns O [b, S, Hq, d],
-    LSE [b, Hq, S], dropped [b, Hq, S] and closest [b, Hq, S]."""
+    pages' setting: the skip inside dense attention).  Returns O [b, S, Hq, dv]
+    (V's width), LSE [b, Hq, S], dropped [b, Hq, S] and closest [b, Hq, S]."""
     lam = _blasst_check(lam)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -473,7 +473,7 @@ def blasst_attention(q, k, v, block_mask, block, lam, softmax_scale=None):
     group = Hq // k.shape[2]
     nb = S // block
     tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    o = np.zeros((b, S, Hq, d))
+    o = np.zeros((b, S, Hq, v.shape[-1]))
     lse = np.full((b, Hq, S), -np.inf)
     dropped = np.zeros((b, Hq, S), dtype=np.int64)
     closest = np.full((b, Hq, S), np.inf)
@@ -495,14 +495,14 @@ def blasst_attention(q, k, v, block_mask, block, lam, softmax_scale=None):
 
 def blasst_attention_rows(q, k, v, block_mask, block, lam, rows, softmax_scale=None):
     """blasst_attention evaluated only at the (batch, head, token) triples in
-    `rows` (block_mask as for attention_rows).  Returns O [rows, d], LSE,
-    dropped and closest [rows]."""
+    `rows` (block_mask as for attention_rows).  Returns O [rows, dv] (V's
+    width), LSE, dropped and closest [rows]."""
     lam = _blasst_check(lam)
     S, Hq, d = q.shape[1], q.shape[2], q.shape[3]
     group = Hq // k.shape[2]
     nb = S // block
     tau = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    out_o = np.zeros((len(rows), d))
+    out_o = np.zeros((len(rows), v.shape[-1]))
     out_l = np.zeros(len(rows))
     out_d = np.zeros(len(rows), dtype=np.int64)
     out_c = np.zeros(len(rows))

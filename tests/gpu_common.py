@@ -91,28 +91,45 @@ def near_tie_diff(gpu_mask, oracle_scores, budget, tol=1e-4):
     return differing, bad
 
 
-def output_error(o_gpu: torch.Tensor, o_ref: np.ndarray):
+def output_error(o_gpu: torch.Tensor, o_ref: np.ndarray, magnitude=None):
     """Max |O_gpu - O_ref| after allowing for the output's own rounding to its
-    storage type (half a bf16 ulp of the reference value)."""
+    storage type (half a bf16 ulp of the reference value), each row divided by
+    its magnitude (see split_magnitude) when one is given."""
     og = o_gpu.float().cpu().numpy().astype(np.float64)
     err = np.abs(og - o_ref)
     if o_gpu.dtype == torch.bfloat16:
         mag = np.maximum(np.abs(o_ref), 2.0 ** -126)
         half_ulp = np.ldexp(1.0, np.floor(np.log2(mag)).astype(np.int64) - 8)
         err = np.maximum(err - half_ulp, 0.0)
+    if magnitude is not None:
+        err = err / np.asarray(magnitude, dtype=np.float64)[..., None]
     return float(err.max()) if err.size else 0.0
 
 
 # Max-abs output tolerances at unit-variance inputs.
 TOL_O = {"f32": 1e-4, "bf16": 1e-2, "fp8": 6e-2}
-
-
-def tol_o(w: wl.Workload, gen_device=None) -> float:
-    """Output tolerance for workload w.  The fp8 bound holds at unit-variance
-    inputs; the fp8 path's error comes from rounding P to E4M3 and O is linear
-    in V, so with V rows scaled by s_t the bound scales by max_t s_t."""
-    if w.dtype != "fp8" or w.v_sigma == 0.0:
-        return TOL_O[w.dtype]
-    return TOL_O["fp8"] * float(wl.v_row_scale(w, gen_device).max())
 TOL_LSE = {"f32": 1e-4, "bf16": 1e-3, "fp8": 1e-3}
 TOL_SCORE = 1e-4
+
+
+def with_scale_column(w: wl.Workload, v64: np.ndarray, gen_device=None) -> np.ndarray:
+    """The oracle's V ([b, S, H, d] fp64) with one more column: the per-token
+    V-row scale s_t the inputs were drawn with (1 for every token when
+    v_sigma = 0).  Attention over it returns in that column each row's
+    softmax-weighted mean of the scales of the V rows it attends to."""
+    sc = wl.v_row_scale(w, gen_device).cpu().double().numpy()           # [b, S]
+    col = np.broadcast_to(sc[:, :, None, None], v64.shape[:-1] + (1,))
+    return np.concatenate([v64, col], axis=-1)
+
+
+def split_magnitude(w: wl.Workload, o_aug: np.ndarray):
+    """(O, magnitude) from attention over with_scale_column's V.  The fp8 bar
+    is stated for unit-variance V.  O is linear in V, and the error of rounding
+    P is a weighted sum over the V rows a row attends to, so with V rows scaled
+    by s_j a row's bound scales by its weighted mean scale S_i = sum_j w_ij s_j:
+    the magnitude is max(1, S_i) for fp8, and 1 otherwise (bf16 and fp32 keep
+    their bars unscaled)."""
+    o, s = o_aug[..., :-1], o_aug[..., -1]
+    if w.dtype == "fp8":
+        return o, np.maximum(1.0, s)
+    return o, np.ones_like(s)

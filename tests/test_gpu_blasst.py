@@ -21,7 +21,8 @@ import torch
 import block_sparse_attention_24_amd as sb
 import oracle
 import workloads as wl
-from gpu_common import TOL_LSE, kv_args, mask_bits, oracle_qkv, output_error, problem, tol_o
+from gpu_common import (TOL_LSE, TOL_O, kv_args, mask_bits, oracle_qkv, output_error, problem, split_magnitude,
+                        with_scale_column)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,16 +51,20 @@ def _words(m):
     return torch.from_numpy(oracle.pack_block_mask(m).view(np.int32)).to(DEV)
 
 
-def _compare(w, o, lse, skipped, o_ref, l_ref, d_ref, closest):
+def _compare(w, o, lse, skipped, o_aug, l_ref, d_ref, closest):
     """O, LSE and dropped counts on the rows whose decisions are clear of the
-    threshold; returns the share of rows left out."""
+    threshold; returns the share of rows left out.  o_aug: the oracle's O over
+    V with the V-row scale column (the row magnitudes of the fp8 bar)."""
+    o_ref, mag = split_magnitude(w, o_aug)
     keep = closest >= SKIP_TIE                                  # [b, Hq, S]
     share = 1.0 - keep.mean()
     print(f"  rows near the threshold: {share:.4%}; dropped per row: mean {d_ref.mean():.2f}", flush=True)
     assert share < 0.02
     b_i, h_i, t_i = np.nonzero(keep)
     og = o[b_i, t_i, h_i]
-    assert output_error(og, o_ref[b_i, t_i, h_i]) < tol_o(w)
+    err = output_error(og, o_ref[b_i, t_i, h_i], mag[b_i, t_i, h_i])
+    print(f"  O error / row magnitude: {err:.4f} (bar {TOL_O[w.dtype]})", flush=True)
+    assert err < TOL_O[w.dtype]
     lg = lse.cpu().double().numpy()[b_i, h_i, t_i]
     assert np.max(np.abs(lg - l_ref[b_i, h_i, t_i])) < TOL_LSE[w.dtype]
     sg = skipped.cpu().numpy()
@@ -103,8 +108,9 @@ def test_blasst_equals_oracle(case):
         _announce(f"blasst {w.name} lambda={lam}")
         o, lse, skipped = sb.attention_blasst(p, inp["q"], k, v, lam, words, table, page)
         torch.cuda.synchronize()
-        o_ref, l_ref, d_ref, closest = oracle.blasst_attention(q64, k64, v64, m_ref, w.block, lam)
-        _compare(w, o, lse, skipped, o_ref, l_ref, d_ref, closest)
+        o_aug, l_ref, d_ref, closest = oracle.blasst_attention(q64, k64, with_scale_column(w, v64), m_ref,
+                                                               w.block, lam)
+        _compare(w, o, lse, skipped, o_aug, l_ref, d_ref, closest)
         if w.sink_logit > 0:
             kept = (np.tril(np.ones((w.num_blocks,) * 2, dtype=bool)) if m_ref is None
                     else m_ref[0, 0]).sum(axis=1)
@@ -168,11 +174,12 @@ def test_blasst_empty_rows_and_null_outputs():
     assert torch.all(torch.isneginf(lse[0, 0, rows]))
     assert torch.all(skipped[0, 0, rows] == 0)
     q64, k64, v64 = oracle_qkv(inp)
-    o_ref, l_ref, d_ref, closest = oracle.blasst_attention(q64, k64, v64, m, w.block, 0.3)
+    o_aug, l_ref, d_ref, closest = oracle.blasst_attention(q64, k64, with_scale_column(w, v64), m, w.block, 0.3)
+    o_ref, mag = split_magnitude(w, o_aug)
     fin = np.isfinite(l_ref)
     keep = (closest >= SKIP_TIE) & fin
     b_i, h_i, t_i = np.nonzero(keep)
-    assert output_error(o[b_i, t_i, h_i], o_ref[b_i, t_i, h_i]) < tol_o(w)
+    assert output_error(o[b_i, t_i, h_i], o_ref[b_i, t_i, h_i], mag[b_i, t_i, h_i]) < TOL_O[w.dtype]
     assert np.array_equal(skipped.cpu().numpy()[keep], d_ref[keep])
 
 
@@ -200,13 +207,14 @@ def test_blasst_full_128k_sampled():
         vh = oracle.dequantize(wl.to_float64(inp["v"][:, :, g:g + 1]), inp["v_scale"])
         m_h = mask_bits(words[:, h:h + 1], nb)
         toks = sorted({0, 5, 127, 128, w.seq - 1} | set(int(x) for x in rng.integers(0, w.seq, 16)))
-        o_ref, l_ref, d_ref, closest = oracle.blasst_attention_rows(
-            qh, kh, vh, m_h, w.block, lam, [(0, 0, t) for t in toks])
+        o_aug, l_ref, d_ref, closest = oracle.blasst_attention_rows(
+            qh, kh, with_scale_column(w, vh, DEV), m_h, w.block, lam, [(0, 0, t) for t in toks])
+        o_ref, mag = split_magnitude(w, o_aug)
         keep = closest >= SKIP_TIE
         near += int((~keep).sum())
         checked += len(toks)
         t_k = [t for t, kk in zip(toks, keep) if kk]
-        assert output_error(o[0, t_k, h], o_ref[keep]) < tol_o(w, DEV), h
+        assert output_error(o[0, t_k, h], o_ref[keep], mag[keep]) < TOL_O[w.dtype], h
         assert np.max(np.abs(lse[0, h, t_k].cpu().double().numpy() - l_ref[keep])) < TOL_LSE[w.dtype], h
         assert np.array_equal(skipped[0, h, t_k].cpu().numpy(), d_ref[keep]), h
     print(f"  rows near the threshold: {near} of {checked}", flush=True)

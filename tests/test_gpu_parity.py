@@ -8,7 +8,10 @@ Bars:
     oracle's fp64 scores except at near-ties (|delta score| < 1e-4);
   * attention, computed on the oracle's mask: max |O - O_ref| within 1e-2
     (bf16), 6e-2 (fp8) or 1e-4 (fp32 inputs), beyond the output's own
-    rounding to bf16; LSE within 1e-3 (1e-4 for fp32).
+    rounding to bf16; LSE within 1e-3 (1e-4 for fp32).  The fp8 bar holds
+    exactly at unit-variance V; where the recipe scales each V row by s_j,
+    each row's bar is 6e-2 * max(1, S_i), S_i = sum_j w_ij s_j its
+    softmax-weighted mean V-row scale (O is linear in V).
 Small shapes get the whole oracle; the full-size workloads are checked on
 sampled rows.  Every case prints its name before it touches the GPU."""
 
@@ -24,8 +27,8 @@ import torch
 import block_sparse_attention_24_amd as sb
 import oracle
 import workloads as wl
-from gpu_common import (TOL_LSE, TOL_O, TOL_SCORE, mask_bits, near_tie_diff, oracle_qkv,
-                        output_error, problem, run_path, tol_o, workspace_views, kv_args)
+from gpu_common import (TOL_LSE, TOL_O, TOL_SCORE, mask_bits, near_tie_diff, oracle_qkv, output_error,
+                        problem, run_path, split_magnitude, with_scale_column, workspace_views, kv_args)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,27 +121,32 @@ def test_small_full_oracle(w):
     k_, v_, table, page = kv_args(w, inp)
     o, lse = sb.attention(p, inp["q"], k_, v_, words, table, page)
     torch.cuda.synchronize()
-    o_ref, lse_ref = oracle.block_sparse_attention(q, k, v, m_ref, w.block)
-    assert output_error(o, o_ref) < tol_o(w)
+    o_aug, lse_ref = oracle.block_sparse_attention(q, k, with_scale_column(w, v), m_ref, w.block)
+    o_ref, mag = split_magnitude(w, o_aug)
+    err = output_error(o, o_ref, mag)
+    print(f"  O error / row magnitude: {err:.4f} (bar {TOL_O[w.dtype]})", flush=True)
+    assert err < TOL_O[w.dtype]
     assert np.max(np.abs(lse.cpu().double().numpy() - lse_ref)) < TOL_LSE[w.dtype]
 
 
-# fp8 at unit-variance inputs (no sink scaling, V rows unscaled): the bar of
-# max-abs 6e-2 applies as stated.  Both fp8 kernels (d = 128 with 128-token
-# blocks, and the other shapes), paged and contiguous, several seeds.
+# fp8 at unit-variance V: the bar of max-abs 6e-2 applies as stated.  Both
+# fp8 kernels (d = 128 with 128-token blocks, and the other shapes), paged and
+# contiguous, eight seeds each without and with the recipe's x4 sink keys
+# (where a few keys carry most of a row's weight, so rounding P matters most).
 FP8_UNIT = [
-    wl.Workload(f"fp8-unit-s{s}-b{blk}-d{d}{'-paged' if paged else ''}", 1, blk * n, hq, hkv, d, blk, "fp8",
-                density=dens, sink=False, v_sigma=0.0, paged=paged, page_size=64, seed=s)
+    wl.Workload(f"fp8-unit{'-sink' if sink else ''}-s{s}-b{blk}-d{d}{'-paged' if paged else ''}", 1, blk * n,
+                hq, hkv, d, blk, "fp8", density=dens, sink=sink, v_sigma=0.0, paged=paged, page_size=64, seed=s)
+    for sink, first in ((False, 11), (True, 31))
     for s, (blk, d, n, hq, hkv, dens, paged) in enumerate([
         (128, 128, 40, 8, 1, 0.25, True), (128, 128, 33, 8, 2, 0.4, False), (128, 128, 48, 4, 2, 0.25, True),
         (128, 128, 24, 8, 2, 0.7, False), (128, 128, 56, 8, 1, 0.3, True), (64, 64, 50, 4, 2, 0.25, False),
-        (128, 64, 33, 2, 2, 0.25, False), (64, 128, 41, 4, 1, 0.4, False)], start=11)]
+        (128, 64, 33, 2, 2, 0.25, False), (64, 128, 41, 4, 1, 0.4, False)], start=first)]
 
 
 @pytest.mark.parametrize("w", FP8_UNIT, ids=lambda w: w.name)
 def test_fp8_unit_variance_bar(w):
     _announce(f"fp8 unit-variance {w.name}")
-    assert tol_o(w) == TOL_O["fp8"]
+    assert w.v_sigma == 0.0                                # unit-variance V: the bar as stated
     inp = wl.make_inputs(w, device=DEV)
     q, k, v = oracle_qkv(inp)
     nb = w.num_blocks
@@ -149,7 +157,9 @@ def test_fp8_unit_variance_bar(w):
     o, lse = sb.attention(problem(w, inp), inp["q"], k_, v_, words, table, page)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.block_sparse_attention(q, k, v, m_ref, w.block)
-    assert output_error(o, o_ref) < TOL_O["fp8"]
+    err = output_error(o, o_ref)
+    print(f"  fp8 O error {err:.4f} (bar {TOL_O['fp8']})", flush=True)
+    assert err < TOL_O["fp8"]
     assert np.max(np.abs(lse.cpu().double().numpy() - lse_ref)) < TOL_LSE["fp8"]
 
 
@@ -169,9 +179,13 @@ def test_dense_kernel_equals_oracle_and_full_mask(w):
     assert np.all(mask_bits(full, nb) == np.tril(np.ones((nb, nb), dtype=bool)))
     assert torch.equal(o_d, o_s) and torch.equal(l_d, l_s)
     q, k, v = oracle_qkv(inp)
-    o_ref, l_ref = oracle.dense_causal_attention(q, k, v) if w.seq <= 2048 else \
-        oracle.block_sparse_attention(q, k, v, np.ones((w.batch, w.hq, nb, nb), dtype=bool), w.block)
-    assert output_error(o_d, o_ref) < tol_o(w)
+    o_aug, l_ref = oracle.block_sparse_attention(q, k, with_scale_column(w, v),
+                                                 np.ones((w.batch, w.hq, nb, nb), dtype=bool), w.block)
+    o_ref, mag = split_magnitude(w, o_aug)
+    if w.seq <= 2048:                                   # the plain dense definition agrees
+        o_pl, l_pl = oracle.dense_causal_attention(q, k, v)
+        assert np.max(np.abs(o_pl - o_ref)) < 1e-12 and np.max(np.abs(l_pl - l_ref)) < 1e-12
+    assert output_error(o_d, o_ref, mag) < TOL_O[w.dtype]
     assert np.max(np.abs(l_d.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
 
 
@@ -225,8 +239,9 @@ def test_empty_rows_and_bits_above_diagonal(w):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     q, k, v = oracle_qkv(inp)
-    o_ref, l_ref = oracle.block_sparse_attention(q, k, v, m, w.block)
-    assert output_error(o1, o_ref) < tol_o(w)
+    o_aug, l_ref = oracle.block_sparse_attention(q, k, with_scale_column(w, v), m, w.block)
+    o_ref, mag = split_magnitude(w, o_aug)
+    assert output_error(o1, o_ref, mag) < TOL_O[w.dtype]
     lg = l1.cpu().double().numpy()
     assert np.all(np.isneginf(lg[0, 0, 4 * 128:5 * 128])) and np.all(np.isneginf(lg[0, 1, :128]))
     fin = np.isfinite(l_ref)
@@ -338,6 +353,8 @@ def _sampled_check(w, inp, out, rows_per_head=12, heads=4, seed=0, gen_device=DE
     budget, total = oracle.tpd_budget(nb, w.density, w.alpha)
     m_gpu_all = out["mask"]
     rows = []
+    errs = []
+    near = 0
     for h in hs:
         g = h // G
         qh = oracle.dequantize(wl.to_float64(q_all[:, :, h:h + 1]), inp["q_scale"])
@@ -350,17 +367,26 @@ def _sampled_check(w, inp, out, rows_per_head=12, heads=4, seed=0, gen_device=DE
         m_gpu = mask_bits(m_gpu_all[:, h:h + 1], nb)
         assert np.array_equal(m_gpu, oracle.select_blocks(s_gpu[:, None], budget)), h
         assert m_gpu.sum() == w.batch * total
+        # against the fp64 scores: differences only at near-ties
+        differing, bad = near_tie_diff(m_gpu, s_ref[:, None], budget)
+        assert not bad, (h, bad[:10])
+        near += differing
         toks = {0, w.seq - 1, (nb // 2) * w.block, w.seq - w.block}
         toks |= set(int(x) for x in rng.integers(0, w.seq, rows_per_head))
         for t in sorted(toks):
             rows.append((0, h, t))
         # attention rows of this head
         sub = [(0, 0, t) for (_, hh, t) in rows if hh == h]
-        o_ref, l_ref = oracle.attention_rows(qh, kh, vh, m_gpu, w.block, sub)
+        o_aug, l_ref = oracle.attention_rows(qh, kh, with_scale_column(w, vh, gen_device), m_gpu, w.block, sub)
+        o_ref, mag = split_magnitude(w, o_aug)
         o_g = out["o"][0, [t for (_, _, t) in sub], h]
         l_g = out["lse"][0, h, [t for (_, _, t) in sub]]
-        assert output_error(o_g, o_ref) < tol_o(w, gen_device), h
+        err = output_error(o_g, o_ref, mag)
+        errs.append(err)
+        assert err < TOL_O[w.dtype], h
         assert np.max(np.abs(l_g.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype], h
+    print(f"  heads {hs}: near-tie rows {near} of {len(hs) * w.batch * nb}; "
+          f"max O error / row magnitude {max(errs):.4f} (bar {TOL_O[w.dtype]})", flush=True)
 
 
 @pytest.mark.parametrize("w", [wl.GQA_8K], ids=lambda w: w.name)
@@ -384,8 +410,9 @@ def test_full_8k_whole_oracle(w):
     words = torch.from_numpy(oracle.pack_block_mask(m_ref).view(np.int32)).to(DEV)
     o, lse = sb.attention(out["p"], inp["q"], inp["k"], inp["v"], words)
     torch.cuda.synchronize()
-    o_ref, l_ref = oracle.block_sparse_attention(q, k, v, m_ref, w.block)
-    assert output_error(o, o_ref) < tol_o(w)
+    o_aug, l_ref = oracle.block_sparse_attention(q, k, with_scale_column(w, v), m_ref, w.block)
+    o_ref, mag = split_magnitude(w, o_aug)
+    assert output_error(o, o_ref, mag) < TOL_O[w.dtype]
     assert np.max(np.abs(lse.cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
 
 
@@ -406,9 +433,22 @@ def test_full_size_sampled(w):
     kh = oracle.dequantize(wl.to_float64(inp["k"][:, :, g:g + 1]), inp["k_scale"])
     vh = oracle.dequantize(wl.to_float64(inp["v"][:, :, g:g + 1]), inp["v_scale"])
     toks = [0, 1, 127, 128, w.seq // 2 + 5, w.seq - 1]
-    o_ref, l_ref = oracle.attention_rows(qh, kh, vh, None, w.block, [(0, 0, t) for t in toks])
-    assert output_error(o_d[0, toks, h], o_ref) < tol_o(w, DEV)
+    o_aug, l_ref = oracle.attention_rows(qh, kh, with_scale_column(w, vh, DEV), None, w.block,
+                                         [(0, 0, t) for t in toks])
+    o_ref, mag = split_magnitude(w, o_aug)
+    assert output_error(o_d[0, toks, h], o_ref, mag) < TOL_O[w.dtype]
     assert np.max(np.abs(l_d[0, h, toks].cpu().double().numpy() - l_ref)) < TOL_LSE[w.dtype]
+
+
+def test_fp8_unit_variance_full_128k():
+    """The 128K fp8 paged configuration at full size with unit-variance V
+    (the x4 sink keys kept), in the bench's launch configuration: sampled
+    rows of sampled heads held to 6e-2 exactly."""
+    w = dataclasses.replace(wl.GQA_128K_FP8_PAGED, name="128k-fp8-paged-unit-v", v_sigma=0.0)
+    _announce(f"full {w.name}")
+    inp = wl.make_inputs(w, device=DEV, gen_device=DEV)
+    out = run_path(w, inp)
+    _sampled_check(w, inp, out, rows_per_head=16, heads=6, seed=3)
 
 
 def test_density_sweep_64k_sampled():

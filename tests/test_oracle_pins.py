@@ -526,6 +526,44 @@ def test_attention_rows_matches_full():
         assert np.max(np.abs(od[n] - o2[bi, i, h])) < 1e-13
 
 
+def test_value_width_is_free_and_weights_sum_to_one():
+    """The attention output has V's width, column by column: with V widened
+    by an all-ones column, that column is exactly the sum of the softmax
+    weights, 1 (0 on a row that sees no key), and the other columns equal the
+    output for V alone.  Holds for the full and the row-sampled oracle, with
+    and without the online skip."""
+    b, S, hq, hkv, d, B = 1, 96, 4, 2, 8, 16
+    q, k, v = _rand_qkv(12, b, S, hq, hkv, d)
+    k[:, :2] *= 3.0
+    nb = S // B
+    rng = np.random.default_rng(12)
+    bm = rng.random((b, hq, nb, nb)) < 0.6
+    bm[0, 1, 3] = False                                   # query block 3 of head 1 sees nothing
+    v1 = np.concatenate([v, np.ones(v.shape[:-1] + (1,))], axis=-1)
+    rows = [(0, 0, 0), (0, 3, 95), (0, 1, 50), (0, 2, 63), (0, 1, 3 * B + 5)]
+    for lam in (None, 0.1):
+        if lam is None:
+            o, lse = oracle.block_sparse_attention(q, k, v, bm, B)
+            o1, _ = oracle.block_sparse_attention(q, k, v1, bm, B)
+            r, rl = oracle.attention_rows(q, k, v, bm, B, rows)
+            r1, _ = oracle.attention_rows(q, k, v1, bm, B, rows)
+        else:
+            o, lse = oracle.blasst_attention(q, k, v, bm, B, lam)[:2]
+            o1 = oracle.blasst_attention(q, k, v1, bm, B, lam)[0]
+            r, rl = oracle.blasst_attention_rows(q, k, v, bm, B, lam, rows)[:2]
+            r1 = oracle.blasst_attention_rows(q, k, v1, bm, B, lam, rows)[0]
+        assert o1.shape == (b, S, hq, d + 1) and r1.shape == (len(rows), d + 1)
+        assert np.array_equal(o1[..., :d], o) and np.array_equal(r1[:, :d], r)
+        empty = np.isneginf(lse).transpose(0, 2, 1)            # [b, S, Hq]: rows that see no key
+        assert empty[0, 3 * B:4 * B, 1].all() and not empty.all()
+        assert np.all(o1[..., d][empty] == 0.0)
+        assert np.max(np.abs(o1[..., d][~empty] - 1.0)) < 1e-14
+        r_empty = np.isneginf(rl)
+        assert r_empty[-1] and not r_empty.all()
+        assert np.all(r1[r_empty, d] == 0.0)
+        assert np.max(np.abs(r1[~r_empty, d] - 1.0)) < 1e-14
+
+
 # --------------------------------------------------------------------------
 # Decode
 # --------------------------------------------------------------------------
