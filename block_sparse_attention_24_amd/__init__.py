@@ -9,7 +9,8 @@ Entry points mirror the C names:
   stem_score_workspace_size, stem_score, stem_score_sam, stem_score_pooled,
   stem_cache_write, stem_tpd_budget, stem_select, bsa_prefill,
   bsa_prefill_blasst, stem_decode_workspace_size, stem_decode,
-  stem_decode_blasst_workspace_size, stem_decode_blasst, stem_last_error
+  stem_decode_blasst_workspace_size, stem_decode_blasst, stem_validate_block_table,
+  stem_validate_lists, stem_last_error
 plus allocating conveniences ``score``, ``score_pooled``, ``cache_write``,
 ``select``, ``attention``, ``attention_blasst``, ``decode`` and ``decode_blasst``.
 """
@@ -30,11 +31,13 @@ STEM_OK, STEM_EINVAL, STEM_EUNSUPPORTED, STEM_EHIP, STEM_EWORKSPACE = 0, -1, -2,
 STEM_F32, STEM_BF16, STEM_FP8_E4M3 = 0, 1, 2
 _DTYPES = {"f32": STEM_F32, "bf16": STEM_BF16, "fp8": STEM_FP8_E4M3}
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+# the block mask is 32-bit words: int32 tensors (torch's usual) or uint32
+_MASK = (torch.int32, torch.uint32)
 
 EXPORTS = ("stem_score_workspace_size", "stem_score", "stem_score_sam", "stem_score_pooled",
            "stem_cache_write", "stem_tpd_budget", "stem_select", "bsa_prefill", "bsa_prefill_blasst",
            "stem_decode_workspace_size", "stem_decode", "stem_decode_blasst_workspace_size",
-           "stem_decode_blasst", "stem_last_error")
+           "stem_decode_blasst", "stem_validate_block_table", "stem_validate_lists", "stem_last_error")
 
 
 class StemError(RuntimeError):
@@ -85,6 +88,8 @@ def lib() -> ctypes.CDLL:
         h.stem_decode_blasst_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
         h.stem_decode_blasst.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, P, P, D,
                                          P, P, P, P, SZ, P]
+        h.stem_validate_block_table.argtypes = [P, I32, I32, I32, I32, I32]
+        h.stem_validate_lists.argtypes = [P, P, I32, I32, I32]
         h.stem_last_error.argtypes = []
         h.stem_last_error.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
@@ -127,8 +132,25 @@ class Problem:
                         self.k_scale, self.v_scale, self.softmax_scale)
 
 
-def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel: int = 0, required: bool = True):
+    """Device address of tensor t, after checking what the C call reads from
+    it: a contiguous GPU tensor of the given dtype(s) with at least `numel`
+    elements.  None passes through as NULL unless the argument is required."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (a strided view would be read as if it were)")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {' or '.join(str(x) for x in allowed)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the call reads or writes {numel}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
@@ -137,11 +159,39 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _kv(k, v, block_table=None, page_size=0):
+def _elem(p: Problem):
+    """torch dtype of Q, K and V for the problem's element type."""
+    return _TORCH[p.dtype]
+
+
+def _out_dtype(p: Problem):
+    return torch.float32 if p.dtype == "f32" else torch.bfloat16
+
+
+def _kv(p: Problem, k, v, block_table=None, page_size=0, dtype=None):
+    """stem_kv_desc for contiguous [b, S, Hkv, d] K/V, or paged
+    [num_pages, page_size, Hkv, d] K/V with an int32 [b, pages_per_seq] table."""
+    dt = _elem(p) if dtype is None else dtype
+    row = p.num_kv_heads * p.head_dim
     if block_table is None:
-        return KvDesc(k.data_ptr(), v.data_ptr(), None, 0, 0, 0)
-    return KvDesc(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), page_size,
+        n = p.batch * p.seq_len * row
+        return KvDesc(_ptr(k, "k", dt, n).value, _ptr(v, "v", dt, n).value, None, 0, 0, 0)
+    if block_table.dim() != 2 or block_table.shape[0] != p.batch:
+        raise ValueError("block_table must be [batch, pages_per_seq]")
+    if k.dim() != 4 or k.shape[1] != page_size or v.shape != k.shape:
+        raise ValueError("paged k and v must be [num_pages, page_size, num_kv_heads, head_dim]")
+    n = k.shape[0] * page_size * row
+    tbl = _ptr(block_table, "block_table", torch.int32, block_table.numel())
+    return KvDesc(_ptr(k, "k", dt, n).value, _ptr(v, "v", dt, n).value, tbl.value, page_size,
                   block_table.shape[1], k.shape[0])
+
+
+def _sizes(p: Problem):
+    """Element counts of the tensors the entry points read or write."""
+    b, S, hq, hkv, d, nb = p.batch, p.seq_len, p.num_q_heads, p.num_kv_heads, p.head_dim, p.num_blocks
+    return dict(q=b * S * hq * d, o=b * S * hq * d, lse=b * hq * S, scores=b * hq * nb * nb,
+                mask=b * hq * nb * p.mask_words, count=b * hq * nb, kbar=b * hkv * nb * d, lvn=b * hkv * nb,
+                kv_in=b * S * hkv * d, dq=b * hq * d, drow=b * hq)
 
 
 # ---- C entry points --------------------------------------------------------
@@ -155,34 +205,43 @@ def stem_score_workspace_size(p: Problem) -> int:
 
 def stem_score(p: Problem, q, k, v, scores, workspace, block_table=None, page_size=0, stream=None):
     d = p.desc()
-    kv = _kv(k, v, block_table, page_size)
-    _check(lib().stem_score(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(scores),
-                            _ptr(workspace), workspace.numel() * workspace.element_size(),
-                            _stream(stream)))
+    n = _sizes(p)
+    kv = _kv(p, k, v, block_table, page_size)
+    _check(lib().stem_score(ctypes.byref(d), _ptr(q, "q", _elem(p), n["q"]), ctypes.byref(kv),
+                            _ptr(scores, "scores", torch.float32, n["scores"]), _ptr(workspace, "workspace"),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def stem_score_sam(p: Problem, q, k, v, scores, workspace, block_table=None, page_size=0,
                    stream=None):
     d = p.desc()
-    kv = _kv(k, v, block_table, page_size)
-    _check(lib().stem_score_sam(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(scores),
-                                _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _stream(stream)))
+    n = _sizes(p)
+    kv = _kv(p, k, v, block_table, page_size)
+    _check(lib().stem_score_sam(ctypes.byref(d), _ptr(q, "q", _elem(p), n["q"]), ctypes.byref(kv),
+                                _ptr(scores, "scores", torch.float32, n["scores"]), _ptr(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def stem_score_pooled(p: Problem, q, kbar, lvn, scores, workspace, stream=None):
     d = p.desc()
-    _check(lib().stem_score_pooled(ctypes.byref(d), _ptr(q), _ptr(kbar), _ptr(lvn), _ptr(scores),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _stream(stream)))
+    n = _sizes(p)
+    _check(lib().stem_score_pooled(ctypes.byref(d), _ptr(q, "q", _elem(p), n["q"]),
+                                   _ptr(kbar, "kbar", torch.float32, n["kbar"]),
+                                   _ptr(lvn, "lvn", torch.float32, n["lvn"], required=False),
+                                   _ptr(scores, "scores", torch.float32, n["scores"]), _ptr(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def stem_cache_write(p: Problem, k_in, v_in, k_cache, v_cache, kbar, lvn, block_table=None,
                      page_size=0, stream=None):
     d = p.desc()
-    kv = _kv(k_cache, v_cache, block_table, page_size)
-    _check(lib().stem_cache_write(ctypes.byref(d), _ptr(k_in), _ptr(v_in), ctypes.byref(kv),
-                                  _ptr(kbar), _ptr(lvn), _stream(stream)))
+    n = _sizes(p)
+    in_t = torch.float32 if p.dtype == "f32" else torch.bfloat16
+    kv = _kv(p, k_cache, v_cache, block_table, page_size)
+    _check(lib().stem_cache_write(ctypes.byref(d), _ptr(k_in, "k_in", in_t, n["kv_in"]),
+                                  _ptr(v_in, "v_in", in_t, n["kv_in"]), ctypes.byref(kv),
+                                  _ptr(kbar, "kbar", torch.float32, n["kbar"]),
+                                  _ptr(lvn, "lvn", torch.float32, n["lvn"]), _stream(stream)))
 
 
 def stem_tpd_budget(num_blocks: int, density: float, alpha: float = 0.5):
@@ -196,23 +255,35 @@ def stem_tpd_budget(num_blocks: int, density: float, alpha: float = 0.5):
 def stem_select(p: Problem, scores, density, alpha, mask, list_out=None, list_stride=0,
                 count=None, stream=None):
     d = p.desc()
-    _check(lib().stem_select(ctypes.byref(d), _ptr(scores), density, alpha, _ptr(mask),
-                             _ptr(list_out), list_stride, _ptr(count), _stream(stream)))
+    n = _sizes(p)
+    _check(lib().stem_select(ctypes.byref(d), _ptr(scores, "scores", torch.float32, n["scores"]), density, alpha,
+                             _ptr(mask, "mask", _MASK, n["mask"]),
+                             _ptr(list_out, "list", torch.int32, n["count"] * max(list_stride, 0), required=False),
+                             list_stride, _ptr(count, "count", torch.int32, n["count"], required=False),
+                             _stream(stream)))
 
 
 def bsa_prefill(p: Problem, q, k, v, mask, o, lse=None, block_table=None, page_size=0, stream=None):
     d = p.desc()
-    kv = _kv(k, v, block_table, page_size)
-    _check(lib().bsa_prefill(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(mask), _ptr(o),
-                             _ptr(lse), _stream(stream)))
+    n = _sizes(p)
+    kv = _kv(p, k, v, block_table, page_size)
+    _check(lib().bsa_prefill(ctypes.byref(d), _ptr(q, "q", _elem(p), n["q"]), ctypes.byref(kv),
+                             _ptr(mask, "mask", _MASK, n["mask"], required=False),
+                             _ptr(o, "o", _out_dtype(p), n["o"]),
+                             _ptr(lse, "lse", torch.float32, n["lse"], required=False), _stream(stream)))
 
 
 def bsa_prefill_blasst(p: Problem, q, k, v, mask, lam, o, lse=None, skipped=None, block_table=None,
                        page_size=0, stream=None):
     d = p.desc()
-    kv = _kv(k, v, block_table, page_size)
-    _check(lib().bsa_prefill_blasst(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(mask), float(lam),
-                                    _ptr(o), _ptr(lse), _ptr(skipped), _stream(stream)))
+    n = _sizes(p)
+    kv = _kv(p, k, v, block_table, page_size)
+    _check(lib().bsa_prefill_blasst(ctypes.byref(d), _ptr(q, "q", _elem(p), n["q"]), ctypes.byref(kv),
+                                    _ptr(mask, "mask", _MASK, n["mask"], required=False), float(lam),
+                                    _ptr(o, "o", _out_dtype(p), n["o"]),
+                                    _ptr(lse, "lse", torch.float32, n["lse"], required=False),
+                                    _ptr(skipped, "skipped", torch.int32, n["lse"], required=False),
+                                    _stream(stream)))
 
 
 def stem_decode_workspace_size(p: Problem) -> int:
@@ -222,13 +293,23 @@ def stem_decode_workspace_size(p: Problem) -> int:
     return n.value
 
 
+def _decode_args(p: Problem, q, seq_lens, keep, kbar, lvn, o, lse):
+    n = _sizes(p)
+    return (_ptr(q, "q", _elem(p), n["dq"]), _ptr(seq_lens, "seq_lens", torch.int32, p.batch),
+            _ptr(keep, "keep", torch.int32, p.batch, required=False),
+            _ptr(kbar, "kbar", torch.float32, n["kbar"], required=False),
+            _ptr(lvn, "lvn", torch.float32, n["lvn"], required=False),
+            _ptr(o, "o", _out_dtype(p), n["dq"]), _ptr(lse, "lse", torch.float32, n["drow"], required=False))
+
+
 def stem_decode(p: Problem, q, k, v, seq_lens, keep, kbar, lvn, o, lse, workspace,
                 block_table=None, page_size=0, stream=None):
     d = p.desc()
-    kv = _kv(k, v, block_table, page_size)
-    _check(lib().stem_decode(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(seq_lens), _ptr(keep),
-                             _ptr(kbar), _ptr(lvn), _ptr(o), _ptr(lse), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    kv = _kv(p, k, v, block_table, page_size)
+    qa, sl, kp, kb, lv, oa, la = _decode_args(p, q, seq_lens, keep, kbar, lvn, o, lse)
+    _check(lib().stem_decode(ctypes.byref(d), qa, ctypes.byref(kv), sl, kp, kb, lv, oa, la,
+                             _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                             _stream(stream)))
 
 
 def stem_decode_blasst_workspace_size(p: Problem) -> int:
@@ -241,11 +322,31 @@ def stem_decode_blasst_workspace_size(p: Problem) -> int:
 def stem_decode_blasst(p: Problem, q, k, v, seq_lens, keep, kbar, lvn, lam, o, lse, skipped, workspace,
                        block_table=None, page_size=0, stream=None):
     d = p.desc()
-    kv = _kv(k, v, block_table, page_size)
-    _check(lib().stem_decode_blasst(ctypes.byref(d), _ptr(q), ctypes.byref(kv), _ptr(seq_lens), _ptr(keep),
-                                    _ptr(kbar), _ptr(lvn), float(lam), _ptr(o), _ptr(lse), _ptr(skipped),
-                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+    kv = _kv(p, k, v, block_table, page_size)
+    qa, sl, kp, kb, lv, oa, la = _decode_args(p, q, seq_lens, keep, kbar, lvn, o, lse)
+    _check(lib().stem_decode_blasst(ctypes.byref(d), qa, ctypes.byref(kv), sl, kp, kb, lv, float(lam), oa, la,
+                                    _ptr(skipped, "skipped", torch.int32, _sizes(p)["drow"], required=False),
+                                    _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
+
+
+def stem_validate_block_table(table, batch: int, pages_per_seq: int, num_pages: int, seq_len: int,
+                              page_size: int) -> None:
+    """Host-side check of a block table (a CPU int32 tensor or array);
+    raises StemError naming the first entry outside [0, num_pages)."""
+    t = torch.as_tensor(table, dtype=torch.int32).contiguous()
+    _check(lib().stem_validate_block_table(ctypes.c_void_p(t.data_ptr()), batch, pages_per_seq, num_pages,
+                                           seq_len, page_size))
+
+
+def stem_validate_lists(lists, counts, rows: int, num_blocks: int, list_stride: int) -> None:
+    """Host-side check of kept lists and counts in stem_select's layout."""
+    l = torch.as_tensor(lists, dtype=torch.int32).contiguous()
+    c = torch.as_tensor(counts, dtype=torch.int32).contiguous()
+    if l.numel() < rows * num_blocks * list_stride or c.numel() < rows * num_blocks:
+        raise ValueError("lists or counts smaller than rows * num_blocks (* list_stride)")
+    _check(lib().stem_validate_lists(ctypes.c_void_p(l.data_ptr()), ctypes.c_void_p(c.data_ptr()), rows,
+                                     num_blocks, list_stride))
 
 
 def stem_last_error() -> str:

@@ -4,18 +4,21 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <limits>
+#include <vector>
 
 #include "stem_internal.h"
 
 using namespace stem;
 
 namespace {
-
 thread_local char g_err[256] = "";
+}  // namespace
 
-int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+namespace stem {
+
 int fail(int code, const char *fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
@@ -29,9 +32,17 @@ int ok() {
     return STEM_OK;
 }
 
+}  // namespace stem
+
+namespace {
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+}  // namespace
+
+namespace stem {
 
 int check_desc(const stem_attn_desc *d, Shape *s) {
     if (!d) return fail(STEM_EINVAL, "desc is NULL");
@@ -122,8 +133,45 @@ void workspace_layout(const Shape &s, size_t *qbar, size_t *kbar, size_t *lvn, s
     *total = *lvn + align256(nl);
 }
 
-// stem_score and stem_score_sam: pool Q, K (and V) into the workspace, then
-// the score GEMM (with the value term unless sam).
+int score_launch(const Shape &s, const void *q, const KvView *kv, float *scores, void *workspace, bool sam,
+                 hipStream_t st, const char *what) {
+    size_t oq, ok_, ol, total;
+    workspace_layout(s, &oq, &ok_, &ol, &total);
+    char *ws = static_cast<char *>(workspace);
+    float *qbar = reinterpret_cast<float *>(ws + oq);
+    float *kbar = reinterpret_cast<float *>(ws + ok_);
+    float *lvn = sam ? nullptr : reinterpret_cast<float *>(ws + ol);
+    hipError_t e = launch_pool(s, q, kv, qbar, kbar, lvn, st);
+    if (e == hipSuccess) e = launch_score(s, qbar, kbar, lvn, scores, st);
+    return hip_status(e, what);
+}
+
+}  // namespace stem
+
+namespace {
+
+// ---- debug checks (STEM_DEBUG set to anything but "" or "0") ----------------
+// The kernels do not check block-table entries or list indices on the device.
+// In debug mode every entry point that reads a block table copies it to the
+// host first (waiting for the stream) and rejects entries outside
+// [0, num_pages) with STEM_EINVAL before anything is enqueued; stem_select
+// waits for its kernel and checks the lists and counts it wrote.
+bool debug_on() {
+    const char *e = std::getenv("STEM_DEBUG");
+    return e && *e && std::strcmp(e, "0") != 0;
+}
+
+int debug_table(const stem_kv_desc *kv, const Shape &s, hipStream_t st) {
+    if (!debug_on() || !kv->block_table) return STEM_OK;
+    std::vector<int32_t> host((size_t)s.batch * kv->pages_per_seq);
+    hipError_t e = hipMemcpyAsync(host.data(), kv->block_table, host.size() * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_status(e, "STEM_DEBUG: reading the block table");
+    return stem_validate_block_table(host.data(), s.batch, kv->pages_per_seq, kv->num_pages, s.seq,
+                                     kv->page_size);
+}
+
 // Arguments of the attention entry points: shapes, K/V, q and o present, and
 // the limits of the attention kernels (32-bit K/V offsets, pages of at least
 // 16 tokens).
@@ -141,6 +189,16 @@ int check_attention(const stem_attn_desc *desc, const void *q, const stem_kv_des
     return 0;
 }
 
+// The decode kernels read a block's page entries one per lane of a wave, so
+// a block may span at most 64 pages; as for the prefill kernels, pages must
+// hold at least 16 tokens.
+int check_decode_pages(const stem_kv_desc *kv, const KvView &v) {
+    if (v.table && kv->page_size < 16) return fail(STEM_EUNSUPPORTED, "page_size below 16 tokens is not supported");
+    return 0;
+}
+
+// stem_score and stem_score_sam: pool Q, K (and V) into the workspace, then
+// the score GEMM (with the value term unless sam).
 int score_from_kv(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv, float *scores,
                   void *workspace, size_t workspace_bytes, void *stream, bool sam) {
     Shape s;
@@ -154,14 +212,9 @@ int score_from_kv(const stem_attn_desc *desc, const void *q, const stem_kv_desc 
     if (workspace_bytes < total)
         return fail(STEM_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
     if ((rc = hip_precheck())) return rc;
-    char *ws = static_cast<char *>(workspace);
-    float *qbar = reinterpret_cast<float *>(ws + oq);
-    float *kbar = reinterpret_cast<float *>(ws + ok_);
-    float *lvn = sam ? nullptr : reinterpret_cast<float *>(ws + ol);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_pool(s, q, &v, qbar, kbar, lvn, st);
-    if (e == hipSuccess) e = launch_score(s, qbar, kbar, lvn, scores, st);
-    return hip_status(e, sam ? "stem_score_sam launch" : "stem_score launch");
+    if ((rc = debug_table(kv, s, static_cast<hipStream_t>(stream)))) return rc;
+    return score_launch(s, q, &v, scores, workspace, sam, static_cast<hipStream_t>(stream),
+                        sam ? "stem_score_sam launch" : "stem_score launch");
 }
 
 }  // namespace
@@ -218,6 +271,7 @@ int stem_cache_write(const stem_attn_desc *desc, const void *k_in, const void *v
     if ((rc = check_kv(cache, s, &v))) return rc;
     if (!k_in || !v_in || !kbar || !lvn) return fail(STEM_EINVAL, "k_in, v_in, kbar or lvn is NULL");
     if ((rc = hip_precheck())) return rc;
+    if ((rc = debug_table(cache, s, static_cast<hipStream_t>(stream)))) return rc;
     hipError_t e = launch_cache_write(s, k_in, v_in, v, kbar, lvn, static_cast<hipStream_t>(stream));
     return hip_status(e, "stem_cache_write launch");
 }
@@ -250,9 +304,20 @@ int stem_select(const stem_attn_desc *desc, const float *scores, double density,
             return fail(STEM_EINVAL, "list_stride %d is below the largest budget %d", list_stride, kmax);
     }
     if ((rc = hip_precheck())) return rc;
-    hipError_t e = launch_select(s, p, scores, mask, list, list_stride, count,
-                                 static_cast<hipStream_t>(stream));
-    return hip_status(e, "stem_select launch");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_select(s, p, scores, mask, list, list_stride, count, st);
+    if ((rc = hip_status(e, "stem_select launch"))) return rc;
+    if (debug_on() && list && count) {
+        // debug mode: the lists and counts just written, checked on the host
+        const size_t rows = (size_t)s.batch * s.hq * s.nb;
+        std::vector<int32_t> hl(rows * list_stride), hc(rows);
+        e = hipMemcpyAsync(hl.data(), list, hl.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipMemcpyAsync(hc.data(), count, hc.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_status(e, "STEM_DEBUG: reading the kept lists");
+        return stem_validate_lists(hl.data(), hc.data(), s.batch * s.hq, s.nb, list_stride);
+    }
+    return STEM_OK;
 }
 
 int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
@@ -262,6 +327,7 @@ int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *k
     int rc = check_attention(desc, q, kv, o, &s, &v);
     if (rc) return rc;
     if ((rc = hip_precheck())) return rc;
+    if ((rc = debug_table(kv, s, static_cast<hipStream_t>(stream)))) return rc;
     hipError_t e = launch_bsa(s, q, v, mask, o, lse, static_cast<hipStream_t>(stream));
     return hip_status(e, "bsa_prefill launch");
 }
@@ -277,6 +343,7 @@ int bsa_prefill_blasst(const stem_attn_desc *desc, const void *q, const stem_kv_
     if (s.d != 128 || s.blk != 128 || s.dtype == STEM_F32)
         return fail(STEM_EUNSUPPORTED, "the online skip needs head_dim 128, block_size 128 and bf16 or FP8");
     if ((rc = hip_precheck())) return rc;
+    if ((rc = debug_table(kv, s, static_cast<hipStream_t>(stream)))) return rc;
     const float skip_log2 = lambda > 0.0 ? (float)std::log2(lambda) : -std::numeric_limits<float>::infinity();
     hipError_t e = launch_bsa_skip(s, q, v, mask, skip_log2, o, lse, skipped, static_cast<hipStream_t>(stream));
     return hip_status(e, "bsa_prefill_blasst launch");
@@ -300,6 +367,7 @@ int stem_decode(const stem_attn_desc *desc, const void *q, const stem_kv_desc *k
     int rc = check_desc(desc, &s);
     if (rc) return rc;
     if ((rc = check_kv(kv, s, &v))) return rc;
+    if ((rc = check_decode_pages(kv, v))) return rc;
     if (!q || !seq_lens || !o || !workspace) return fail(STEM_EINVAL, "q, seq_lens, o or workspace is NULL");
     if (keep && !kbar) return fail(STEM_EINVAL, "kbar is NULL but keep is given");
     size_t a, b, c, total;
@@ -307,6 +375,7 @@ int stem_decode(const stem_attn_desc *desc, const void *q, const stem_kv_desc *k
     if (workspace_bytes < total)
         return fail(STEM_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
     if ((rc = hip_precheck())) return rc;
+    if ((rc = debug_table(kv, s, static_cast<hipStream_t>(stream)))) return rc;
     hipError_t e = launch_decode(s, q, v, seq_lens, keep, kbar, lvn, o, lse, workspace,
                                  static_cast<hipStream_t>(stream));
     return hip_status(e, "stem_decode launch");
@@ -331,6 +400,7 @@ int stem_decode_blasst(const stem_attn_desc *desc, const void *q, const stem_kv_
     int rc = check_desc(desc, &s);
     if (rc) return rc;
     if ((rc = check_kv(kv, s, &v))) return rc;
+    if ((rc = check_decode_pages(kv, v))) return rc;
     if (!q || !seq_lens || !o || !workspace) return fail(STEM_EINVAL, "q, seq_lens, o or workspace is NULL");
     if (keep && !kbar) return fail(STEM_EINVAL, "kbar is NULL but keep is given");
     if (!(lambda >= 0.0 && lambda <= 1.0)) return fail(STEM_EINVAL, "lambda must lie in [0, 1]");
@@ -339,12 +409,52 @@ int stem_decode_blasst(const stem_attn_desc *desc, const void *q, const stem_kv_
     if (workspace_bytes < total)
         return fail(STEM_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
     if ((rc = hip_precheck())) return rc;
+    if ((rc = debug_table(kv, s, static_cast<hipStream_t>(stream)))) return rc;
     DecodeSkip sk;
     sk.log2_lambda = lambda > 0.0 ? (float)std::log2(lambda) : -std::numeric_limits<float>::infinity();
     sk.skipped = skipped;
     hipError_t e = launch_decode(s, q, v, seq_lens, keep, kbar, lvn, o, lse, workspace,
                                  static_cast<hipStream_t>(stream), &sk);
     return hip_status(e, "stem_decode_blasst launch");
+}
+
+int stem_validate_block_table(const int32_t *table, int32_t batch, int32_t pages_per_seq, int32_t num_pages,
+                              int32_t seq_len, int32_t page_size) {
+    if (!table) return fail(STEM_EINVAL, "table is NULL");
+    if (batch < 1 || seq_len < 1 || num_pages < 1) return fail(STEM_EINVAL, "batch, seq_len and num_pages must be positive");
+    if (page_size < 1 || (page_size & (page_size - 1))) return fail(STEM_EINVAL, "page_size %d is not a power of two", page_size);
+    if ((long long)pages_per_seq * page_size < seq_len) return fail(STEM_EINVAL, "pages_per_seq * page_size < seq_len");
+    const int used = (int)(((long long)seq_len + page_size - 1) / page_size);
+    for (int b = 0; b < batch; ++b)
+        for (int p = 0; p < used; ++p) {
+            const int32_t e = table[(size_t)b * pages_per_seq + p];
+            if (e < 0 || e >= num_pages)
+                return fail(STEM_EINVAL, "block_table[%d][%d] = %d lies outside [0, %d)", b, p, e, num_pages);
+        }
+    return ok();
+}
+
+int stem_validate_lists(const int32_t *lists, const int32_t *counts, int32_t rows_per_block_row, int32_t num_blocks,
+                        int32_t list_stride) {
+    if (!lists || !counts) return fail(STEM_EINVAL, "lists or counts is NULL");
+    if (rows_per_block_row < 1 || num_blocks < 1 || list_stride < 1)
+        return fail(STEM_EINVAL, "row count, num_blocks and list_stride must be positive");
+    for (long long r = 0; r < (long long)rows_per_block_row * num_blocks; ++r) {
+        const int I = (int)(r % num_blocks);
+        const int c = counts[r];
+        if (c < 0 || c > I + 1 || c > list_stride)
+            return fail(STEM_EINVAL, "count of row %lld (query block %d) is %d, outside [0, %d]", r, I, c,
+                        I + 1 < list_stride ? I + 1 : list_stride);
+        const int32_t *l = lists + r * list_stride;
+        for (int e = 0; e < c; ++e) {
+            if (l[e] < 0 || l[e] > I)
+                return fail(STEM_EINVAL, "list of row %lld (query block %d), entry %d = %d lies outside [0, %d]", r,
+                            I, e, l[e], I);
+            if (e > 0 && l[e] <= l[e - 1])
+                return fail(STEM_EINVAL, "list of row %lld is not strictly ascending at entry %d", r, e);
+        }
+    }
+    return ok();
 }
 
 }  // extern "C"

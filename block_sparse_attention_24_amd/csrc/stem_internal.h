@@ -72,6 +72,21 @@ __host__ __device__ inline int tpd_row_budget(const TpdPlan &p, int row) {
     return (int)n;
 }
 
+// Host-side argument handling shared by the entry points (api.cpp).
+// fail: records the message for stem_last_error and returns code; ok: clears it.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int ok();
+int check_desc(const stem_attn_desc *d, Shape *s);
+int check_kv(const stem_kv_desc *kv, const Shape &s, KvView *out);
+int hip_status(hipError_t e, const char *what);
+int hip_precheck();
+// stem_score's workspace: offsets of qbar, kbar, lvn and the total bytes.
+void workspace_layout(const Shape &s, size_t *qbar, size_t *kbar, size_t *lvn, size_t *total);
+// Pools into `workspace` (stem_score's layout) and runs the score GEMM;
+// returns the status of the launches (what names them in the message).
+int score_launch(const Shape &s, const void *q, const KvView *kv, float *scores, void *workspace, bool sam,
+                 hipStream_t st, const char *what);
+
 // Host: builds the plan (validates density/alpha); returns STEM_OK or an error.
 int tpd_make_plan(int nb, double density, double alpha, TpdPlan *out, const char **why);
 

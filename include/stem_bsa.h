@@ -55,7 +55,8 @@
  * Supported shapes: head_dim in {64, 128}; block_size in {64, 128};
  * seq_len a positive multiple of block_size with Nb <= 4096; dtype STEM_F32,
  * STEM_BF16 or STEM_FP8_E4M3 (OCP E4M3, "e4m3fn", with per-tensor fp32
- * scales: real value = code * scale).  Paged K/V: page_size a power of two.
+ * scales: real value = code * scale).  Paged K/V: page_size a power of two;
+ * the attention and decode entry points need at least 16 tokens per page.
  */
 #ifndef STEM_BSA_H
 #define STEM_BSA_H
@@ -97,7 +98,7 @@ typedef struct {
 /* Where K and V live.  block_table == NULL: contiguous [batch, seq_len,
  * num_kv_heads, head_dim] tensors; otherwise paged (layout above) and every
  * block_table entry must lie in [0, num_pages) — entries are not checked on
- * the device. */
+ * the device (see STEM_DEBUG below for a host-side check). */
 typedef struct {
     const void *k;
     const void *v;
@@ -187,7 +188,8 @@ int stem_decode_workspace_size(const stem_attn_desc *desc, size_t *bytes);
  *   q:        [batch, num_q_heads, head_dim] in desc->dtype (FP8 codes with
  *             q_scale).
  *   kv:       the cache (contiguous or paged), holding tokens 0..t of every
- *             sequence, the new token's K and V included.
+ *             sequence, the new token's K and V included.  Paged caches need
+ *             pages of at least 16 tokens (STEM_EUNSUPPORTED otherwise).
  *   seq_lens: device int32 [batch], tokens in each sequence including the new
  *             one; values outside [1, seq_len] are clamped into it.
  *   keep:     device int32 [batch], blocks to keep for the new token's row
@@ -295,6 +297,30 @@ int bsa_prefill(const stem_attn_desc *desc, const void *q, const stem_kv_desc *k
 int bsa_prefill_blasst(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
                        const uint32_t *mask, double lambda, void *o, float *lse, int32_t *skipped,
                        void *stream);
+
+/* Debug checks.  With the environment variable STEM_DEBUG set (to anything
+ * but "" or "0"), every entry point that reads a block table first copies it
+ * to the host, waiting for `stream`, and returns STEM_EINVAL, with nothing
+ * enqueued, when an entry that one of the batch's seq_len tokens uses lies
+ * outside [0, num_pages); stem_select waits for its kernel and checks the
+ * lists and counts it wrote with stem_validate_lists.  Debug mode breaks the
+ * no-synchronisation convention on purpose; it is for finding bad inputs, not
+ * for timing.  The two checks are also callable directly on host arrays.
+ *
+ * stem_validate_block_table: table is HOST int32 [batch, pages_per_seq];
+ * checks entries [b][p] for p < ceil(seq_len / page_size).  STEM_OK, or
+ * STEM_EINVAL naming the first bad entry (or a bad argument). */
+int stem_validate_block_table(const int32_t *table, int32_t batch, int32_t pages_per_seq, int32_t num_pages,
+                              int32_t seq_len, int32_t page_size);
+
+/* stem_validate_lists: lists HOST int32 [rows, num_blocks, list_stride] and
+ * counts HOST int32 [rows, num_blocks] in stem_select's layout (rows = batch *
+ * num_q_heads; the row of query block I is entry I).  Each count must lie in
+ * [0, min(I + 1, list_stride)] and its entries must be strictly ascending
+ * block indices in [0, I].  STEM_OK, or STEM_EINVAL naming the first bad
+ * count or entry. */
+int stem_validate_lists(const int32_t *lists, const int32_t *counts, int32_t rows, int32_t num_blocks,
+                        int32_t list_stride);
 
 /* Message for the last non-OK return on this thread ("" if none). */
 const char *stem_last_error(void);

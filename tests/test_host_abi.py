@@ -288,3 +288,69 @@ def test_decode_blasst_checks():
         assert L.stem_decode_blasst(*args(lam=lam)) == sb.STEM_EINVAL
         assert "lambda" in sb.stem_last_error()
     assert L.stem_decode_blasst(*args(nbytes=n - 1)) == sb.STEM_EWORKSPACE
+
+
+@pytest.mark.parametrize("page", [1, 2, 8])
+def test_decode_rejects_pages_below_16_tokens(page):
+    """The decode kernels hand a block's page entries to its rows one per lane
+    of a wave; pages of fewer than 16 tokens are rejected before any launch,
+    as for the attention entry points."""
+    L = sb.lib()
+    p = sb.Problem(1, 1024, 4, 2, 128, 128, "bf16")
+    d = p.desc()
+    kv = sb.KvDesc(0x1000, 0x1000, 0x2000, page, 1024 // page, 1024 // page)
+    n = sb.stem_decode_blasst_workspace_size(p)
+    assert L.stem_decode(ctypes.byref(d), FAKE, ctypes.byref(kv), FAKE, None, None, None, FAKE, None, FAKE,
+                         n, None) == sb.STEM_EUNSUPPORTED
+    assert "page_size" in sb.stem_last_error()
+    assert L.stem_decode_blasst(ctypes.byref(d), FAKE, ctypes.byref(kv), FAKE, None, None, None, 0.1, FAKE,
+                                None, None, FAKE, n, None) == sb.STEM_EUNSUPPORTED
+    assert L.bsa_prefill(ctypes.byref(d), FAKE, ctypes.byref(kv), None, FAKE, None, None) == sb.STEM_EUNSUPPORTED
+
+
+def test_validate_block_table():
+    """The debug-mode check of a block table, on host arrays: every page the
+    batch's seq_len tokens use must name a page in [0, num_pages)."""
+    import numpy as np
+    t = np.arange(2 * 8, dtype=np.int32).reshape(2, 8)            # 2 sequences, 8 pages each
+    sb.stem_validate_block_table(t, 2, 8, 16, 512, 64)
+    sb.stem_validate_block_table(t, 2, 8, 16, 500, 64)             # a partial last page
+    for bad_at, val in (((0, 3), 16), ((1, 7), -1), ((1, 0), 1 << 30)):
+        u = t.copy()
+        u[bad_at] = val
+        with pytest.raises(sb.StemError, match=rf"block_table\[{bad_at[0]}\]\[{bad_at[1]}\]"):
+            sb.stem_validate_block_table(u, 2, 8, 16, 512, 64)
+    u = t.copy()
+    u[1, 7] = 99                                                    # a page no token uses
+    sb.stem_validate_block_table(u, 2, 8, 16, 448, 64)
+    with pytest.raises(sb.StemError):
+        sb.stem_validate_block_table(t, 2, 8, 16, 513, 64)         # more tokens than pages
+    with pytest.raises(sb.StemError):
+        sb.stem_validate_block_table(t, 2, 8, 16, 512, 48)         # not a power of two
+
+
+def test_validate_lists():
+    """The debug-mode check of stem_select's lists and counts: counts in
+    [0, min(I + 1, stride)], entries strictly ascending in [0, I]."""
+    import numpy as np
+    nb, stride, rows = 6, 3, 2
+    budget, _ = oracle.tpd_budget(nb, 0.5)
+    scores = np.random.default_rng(3).standard_normal((1, rows, nb, nb))
+    m = oracle.select_blocks(scores, budget)
+    lists = np.full((rows, nb, stride), -7, dtype=np.int32)
+    counts = np.zeros((rows, nb), dtype=np.int32)
+    for h in range(rows):
+        for i in range(nb):
+            js = np.nonzero(m[0, h, i])[0]
+            counts[h, i] = len(js)
+            lists[h, i, :len(js)] = js
+    assert counts.max() <= stride
+    sb.stem_validate_lists(lists, counts, rows, nb, stride)
+    for mutate, what in ((lambda l, c: c.__setitem__((1, 2), 4), "count"),
+                         (lambda l, c: c.__setitem__((0, 0), -1), "count"),
+                         (lambda l, c: l.__setitem__((1, 5, 0), 6), "entry"),
+                         (lambda l, c: l.__setitem__((0, 3, 1), l[0, 3, 0]), "ascending")):
+        l2, c2 = lists.copy(), counts.copy()
+        mutate(l2, c2)
+        with pytest.raises(sb.StemError, match=what):
+            sb.stem_validate_lists(l2, c2, rows, nb, stride)
