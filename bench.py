@@ -193,7 +193,8 @@ def time_decode(w: wl.Workload, p, k, v, table, page, ws_score, runs: int):
         with t:
             sb.stem_decode(pd, q, k, v, lens, keep, kbar, lvn, o, lse, ws, table, page)
     torch.cuda.synchronize()
-    ms = sum(t.ms()) / runs
+    st = t.stats()
+    ms = st["mean"]
     es = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     block_bytes = 2 * w.block * w.head_dim * es           # K and V of one block, one KV head
     lists = ws[:w.batch * w.hq * nb * 4].view(torch.int32).view(w.batch, w.hq, nb)
@@ -207,12 +208,13 @@ def time_decode(w: wl.Workload, p, k, v, table, page, ws_score, runs: int):
     union *= block_bytes
     return {
         "decode_ms": ms,
+        "decode_ms_stats": st,
         "kept_blocks_per_head": kept,
-        "kv_bytes_per_head_sum": per_head,
         "kv_bytes_group_union": union,
-        "gbs_per_head_sum": per_head / (ms * 1e-3) / 1e9,
+        "kv_bytes_requested_per_head_sum": per_head,
         "gbs_group_union": union / (ms * 1e-3) / 1e9,
-        "hbm_frac_per_head_sum": per_head / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "hbm_frac_group_union": union / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "gbs_requested_per_head_sum": per_head / (ms * 1e-3) / 1e9,
     }
 
 
@@ -373,6 +375,13 @@ class Timer:
     def ms(self):
         return [a.elapsed_time(b) for a, b in self.pairs]
 
+    def stats(self):
+        """min, median and mean of the event-timed durations (ms)."""
+        x = sorted(self.ms())
+        n = len(x)
+        med = x[n // 2] if n % 2 else 0.5 * (x[n // 2 - 1] + x[n // 2])
+        return {"min": x[0], "median": med, "mean": sum(x) / n, "runs": n}
+
 
 def cpu_baseline(w: wl.Workload, inp, budget, seconds: float = 15.0):
     """The oracle, untuned, on the host cores: OAM scores of head 0, the TPD
@@ -427,11 +436,11 @@ def cpu_baseline(w: wl.Workload, inp, budget, seconds: float = 15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=wl.GQA_128K_FP8_PAGED.name, choices=sorted(WORKLOADS))
     ap.add_argument("--density", type=float, default=None)
-    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--dense-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
@@ -513,8 +522,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
-    sc_ms, se_ms, bsa_ms = (sum(t.ms()) / len(t.ms()) for t in (t_score, t_select, t_bsa))
-    log(f"[bench] step {ms_step:.3f} ms: score {sc_ms:.3f} select {se_ms:.3f} bsa {bsa_ms:.3f}")
+    st_score, st_select, st_bsa = (t.stats() for t in (t_score, t_select, t_bsa))
+    sc_ms, se_ms, bsa_ms = st_score["mean"], st_select["mean"], st_bsa["mean"]
+    log(f"[bench] step {ms_step:.3f} ms: score {sc_ms:.3f} select {se_ms:.3f} bsa {bsa_ms:.3f} "
+        f"(min {st_bsa['min']:.3f}, median {st_bsa['median']:.3f})")
 
     result = {
         "metric": METRIC,
@@ -529,7 +540,10 @@ def main():
         "data": "synthetic",
         "config": w.describe(),
         "stages_ms": {"score": sc_ms, "select": se_ms, "bsa": bsa_ms},
+        "stages_ms_stats": {"score": st_score, "select": st_select, "bsa": st_bsa},
         "bsa_ms": bsa_ms,
+        "bsa_ms_min": st_bsa["min"],
+        "bsa_ms_median": st_bsa["median"],
         "bsa_kept_tflops": kept_flops / (bsa_ms * 1e-3) / 1e12,
         "kept_tflop_per_step": kept_flops / 1e12,
         "score_gbs": score_bytes(w) / (sc_ms * 1e-3) / 1e9,
@@ -541,7 +555,10 @@ def main():
     result["roofline"] = {"bound": "mfma", "kernel": kname + " (sparse)",
                           "achieved": result["bsa_kept_tflops"], "peak": peak, "unit": "TFLOP/s",
                           "frac": result["bsa_kept_tflops"] / peak, "traffic": traffic,
-                          "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
+                          "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                          "traffic_source": ("the summary under profiles/ taken on this attention source "
+                                             "(not measured in this run); null once the source changed"),
+                          "achieved_from": "mean of the HIP-event durations of the timed launches"}
 
     if not args.no_dense:
         log(f"[bench] dense baseline and density-1 sparse run, {args.dense_steps} each")
@@ -557,8 +574,8 @@ def main():
             with t_full:
                 sb.bsa_prefill(p, q, k, v, full, o, lse, table, page)
         torch.cuda.synchronize()
-        dense_ms = sum(t_dense.ms()) / args.dense_steps
-        full_ms = sum(t_full.ms()) / args.dense_steps
+        st_dense, st_full = t_dense.stats(), t_full.stats()
+        dense_ms, full_ms = st_dense["mean"], st_full["mean"]
         rho = kept_flops / dense_flops
         result.update({
             "dense_ms": dense_ms,
@@ -567,6 +584,9 @@ def main():
             "ratio_vs_dense_rho": bsa_ms / (rho * dense_ms),
             "skip_overhead_density1": full_ms / dense_ms - 1.0,
             "density1_sparse_ms": full_ms,
+            "dense_ms_stats": st_dense,
+            "density1_sparse_ms_stats": st_full,
+            "ratio_vs_dense_median": st_bsa["median"] / (w.density * st_dense["median"]),
         })
         log(f"[bench] dense {dense_ms:.3f} ms, density-1 sparse {full_ms:.3f} ms, "
             f"R {result['ratio_vs_dense']:.3f}")
