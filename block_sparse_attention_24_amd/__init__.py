@@ -6,7 +6,7 @@ memory and the current HIP stream.  There is no fallback: if the library is
 missing, every call raises.
 
 Entry points mirror the C names:
-  stem_score_workspace_size, stem_score, stem_score_sam, stem_score_pooled,
+  stem_score_workspace_size, stem_score, stem_score_noalloc, stem_score_sam, stem_score_pooled,
   stem_cache_write, stem_tpd_budget, stem_select, bsa_prefill,
   bsa_prefill_blasst, stem_decode_workspace_size, stem_decode,
   stem_decode_blasst_workspace_size, stem_decode_blasst, stem_validate_block_table,
@@ -28,13 +28,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libstem_bsa.so")
 
 STEM_OK, STEM_EINVAL, STEM_EUNSUPPORTED, STEM_EHIP, STEM_EWORKSPACE = 0, -1, -2, -3, -4
+STEM_NOALLOC_SCRATCH_BYTES = 64 << 20          # include/stem_bsa.h
 STEM_F32, STEM_BF16, STEM_FP8_E4M3 = 0, 1, 2
 _DTYPES = {"f32": STEM_F32, "bf16": STEM_BF16, "fp8": STEM_FP8_E4M3}
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 # the block mask is 32-bit words: int32 tensors (torch's usual) or uint32
 _MASK = (torch.int32, torch.uint32)
 
-EXPORTS = ("stem_score_workspace_size", "stem_score", "stem_score_sam", "stem_score_pooled",
+EXPORTS = ("stem_score_workspace_size", "stem_score", "stem_score_noalloc", "stem_score_sam", "stem_score_pooled",
            "stem_cache_write", "stem_tpd_budget", "stem_select", "bsa_prefill", "bsa_prefill_blasst",
            "stem_decode_workspace_size", "stem_decode", "stem_decode_blasst_workspace_size",
            "stem_decode_blasst", "stem_validate_block_table", "stem_validate_lists", "stem_last_error")
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, D, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
         h.stem_score_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
         h.stem_score.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P, SZ, P]
+        h.stem_score_noalloc.argtypes = [ctypes.POINTER(AttnDesc), P, ctypes.POINTER(KvDesc), P, P]
         h.stem_score_sam.argtypes = h.stem_score.argtypes
         h.stem_score_pooled.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, SZ, P]
         h.stem_cache_write.argtypes = [ctypes.POINTER(AttnDesc), P, P, ctypes.POINTER(KvDesc), P, P, P]
@@ -210,6 +212,14 @@ def stem_score(p: Problem, q, k, v, scores, workspace, block_table=None, page_si
     _check(lib().stem_score(ctypes.byref(d), _ptr(q, "q", _elem(p), n["q"]), ctypes.byref(kv),
                             _ptr(scores, "scores", torch.float32, n["scores"]), _ptr(workspace, "workspace"),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def stem_score_noalloc(p: Problem, q, k, v, scores, block_table=None, page_size=0, stream=None):
+    d = p.desc()
+    n = _sizes(p)
+    kv = _kv(p, k, v, block_table, page_size)
+    _check(lib().stem_score_noalloc(ctypes.byref(d), _ptr(q, "q", _elem(p), n["q"]), ctypes.byref(kv),
+                                    _ptr(scores, "scores", torch.float32, n["scores"]), _stream(stream)))
 
 
 def stem_score_sam(p: Problem, q, k, v, scores, workspace, block_table=None, page_size=0,

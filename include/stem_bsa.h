@@ -133,6 +133,25 @@ int stem_score(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv
 int stem_score_sam(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
                    float *scores, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device scratch stem_score_noalloc holds on each device: room for
+ * stem_score's workspace (stem_score_workspace_size) up to this size, e.g.
+ * 128K tokens with 64 query / 8 KV heads and head_dim 128 (36 MiB). */
+#define STEM_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* stem_score for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels and the same scores, bit for bit; the pooled representations
+ * go to a scratch array the library holds on each device (fixed size,
+ * STEM_NOALLOC_SCRATCH_BYTES, kept until the process ends) instead of a
+ * workspace.  The call allocates nothing.
+ *   stream: must belong to the current device (STEM_EINVAL otherwise).
+ * A problem whose stem_score workspace exceeds STEM_NOALLOC_SCRATCH_BYTES is
+ * rejected with STEM_EWORKSPACE.  All calls on one device share its scratch:
+ * calls that overlap in time on one device (different streams or threads)
+ * race, and the representations are not readable by the caller. */
+int stem_score_noalloc(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
+                       float *scores, void *stream);
+
 /* Block scores from key-block representations computed earlier (by
  * stem_cache_write, or left in a stem_score workspace): pools Q into the qbar
  * region of the workspace, then the score GEMM of stem_score.
