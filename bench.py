@@ -89,12 +89,12 @@ def attn_flops(w: wl.Workload, kept_blocks_per_head: int) -> float:
 
 def score_bytes(w: wl.Workload) -> float:
     """Algorithmic HBM bytes of the scoring pass: read Q, K, V once, write the
-    pooled representations and the score matrix (the GEMM re-reads the pooled
-    rows, a few MiB, not counted)."""
+    pooled representations and the scores on and below the diagonal (the GEMM
+    re-reads the pooled rows, a few MiB, not counted)."""
     es = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     nb = w.num_blocks
     read = w.batch * w.seq * (w.hq + 2 * w.hkv) * w.head_dim * es
-    write = 4 * w.batch * nb * ((w.hq + w.hkv) * w.head_dim + w.hkv) + 4 * w.batch * w.hq * nb * nb
+    write = 4 * w.batch * nb * ((w.hq + w.hkv) * w.head_dim + w.hkv) + 4 * w.batch * w.hq * nb * (nb + 1) // 2
     return float(read + write)
 
 
@@ -110,11 +110,11 @@ def cache_write_bytes(w: wl.Workload) -> float:
 
 def pooled_score_bytes(w: wl.Workload) -> float:
     """Algorithmic HBM bytes of scoring from precomputed kbar/lvn: read Q,
-    kbar and lvn, write qbar and the score matrix."""
+    kbar and lvn, write qbar and the scores on and below the diagonal."""
     es = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     nb = w.num_blocks
     read = w.batch * w.seq * w.hq * w.head_dim * es + 4 * w.batch * w.hkv * nb * (w.head_dim + 1)
-    write = 4 * w.batch * w.hq * nb * (w.head_dim + nb)
+    write = 4 * w.batch * w.hq * nb * w.head_dim + 4 * w.batch * w.hq * nb * (nb + 1) // 2
     return float(read + write)
 
 

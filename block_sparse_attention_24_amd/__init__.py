@@ -367,18 +367,20 @@ def stem_last_error() -> str:
 
 def score(p: Problem, q, k, v, block_table=None, page_size=0, stream=None, sam=False):
     """Returns (scores [b,Hq,Nb,Nb] fp32, workspace bytes as uint8).  sam=True
-    leaves the value term out."""
+    leaves the value term out.  The library writes J <= I only; the returned
+    tensor is filled with -inf above the diagonal."""
     nb = p.num_blocks
-    scores = torch.empty((p.batch, p.num_q_heads, nb, nb), dtype=torch.float32, device=q.device)
+    scores = torch.full((p.batch, p.num_q_heads, nb, nb), float("-inf"), dtype=torch.float32, device=q.device)
     ws = torch.empty(stem_score_workspace_size(p), dtype=torch.uint8, device=q.device)
     (stem_score_sam if sam else stem_score)(p, q, k, v, scores, ws, block_table, page_size, stream)
     return scores, ws
 
 
 def score_pooled(p: Problem, q, kbar, lvn=None, stream=None):
-    """Scores from precomputed kbar/lvn (lvn None: SAM).  Returns (scores, workspace)."""
+    """Scores from precomputed kbar/lvn (lvn None: SAM).  Returns (scores,
+    workspace); -inf above the diagonal, as score() gives."""
     nb = p.num_blocks
-    scores = torch.empty((p.batch, p.num_q_heads, nb, nb), dtype=torch.float32, device=q.device)
+    scores = torch.full((p.batch, p.num_q_heads, nb, nb), float("-inf"), dtype=torch.float32, device=q.device)
     ws = torch.empty(stem_score_workspace_size(p), dtype=torch.uint8, device=q.device)
     stem_score_pooled(p, q, kbar, lvn, scores, ws, stream)
     return scores, ws

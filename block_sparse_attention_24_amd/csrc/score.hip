@@ -9,7 +9,8 @@
 //                       prefill's K and V into the (FP8, paged) cache: one pass
 //                       over the new tokens stores them and pools them.
 //   score_kernel        per head, tau * qbar kbar^T (+ lvn) on the matrix
-//                       cores, -inf above the diagonal.
+//                       cores, on and below the diagonal only (selection
+//                       never reads J > I, so nothing is written there).
 // All use a fixed summation order, so results are bit-reproducible; the cache
 // write accumulates exactly as pool_kernel does over the stored values, so
 // its representations equal, bit for bit, those pooled later from the cache.
@@ -265,8 +266,9 @@ hipError_t pool_all(const Shape &s, const void *q, const KvView *kv, float *qbar
 
 // ---------------------------------------------------------------------------
 // Score GEMM on the matrix cores (v_mfma_f32_32x32x2f32, fp32 in and out).  A
-// workgroup owns a 128 x 128 tile of (I, J), each of its four waves a 64 x 64
-// quarter held as 2 x 2 MFMA tiles.  Per chunk of 8 dimensions a lane loads
+// workgroup owns a 128 x 128 tile of (I, J) on or below the diagonal, each of
+// its four waves a 64 x 64 quarter held as 2 x 2 MFMA tiles; a quarter wholly
+// above the diagonal returns at once, and elements with J > I are not stored.  Per chunk of 8 dimensions a lane loads
 // four consecutive floats of one qbar row and of one kbar row straight from
 // global memory (lanes 0-31 dimensions d0..d0+3, lanes 32-63 d0+4..d0+7), so
 // MFMA step c of the chunk pairs dimension d0+c with d0+4+c.  The order of
@@ -285,46 +287,28 @@ struct ScoreArgs {
 
 template <int D>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-    // XCD-contiguous renumbering of (tile, head, batch)
+    // XCD-contiguous renumbering of (tile, head, batch); the tiles of a head
+    // are the tiles.(tiles+1)/2 on or below the diagonal, numbered row by row
     const unsigned n = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const unsigned total = gridDim.x * gridDim.y * gridDim.z;
     const unsigned m = (total & 7u) ? n : (n & 7u) * (total >> 3) + (n >> 3);
     const int tile = (int)(m % gridDim.x);
     const int h = (int)((m / gridDim.x) % gridDim.y);
     const int b = (int)(m / (gridDim.x * gridDim.y));
-    const int ti = tile / a.tiles, tj = tile % a.tiles;
+    int ti = (int)((__builtin_sqrtf(8.0f * (float)tile + 1.0f) - 1.0f) * 0.5f);
+    while (ti * (ti + 1) / 2 > tile) --ti;              // exact triangular root
+    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
+    const int tj = tile - ti * (ti + 1) / 2;            // 0 <= tj <= ti
     const int g = h / (a.hq / a.hkv);
     const int tid = threadIdx.x;
     float *out = a.scores + ((size_t)b * a.hq + h) * a.nb * a.nb;
-    const float ninf = -__builtin_huge_valf();
 
     const int w = tid >> 6, lane = tid & 63;
     const int r = lane & 31, kh = lane >> 5;
     const int I0 = ti * kTile + (w >> 1) * 64;
     const int J0 = tj * kTile + (w & 1) * 64;
     if (I0 >= a.nb || J0 >= a.nb) return;      // nothing of this quarter is stored
-
-    if (J0 > I0 + 63) {               // this quarter lies wholly above the diagonal
-        if ((a.nb & 3) == 0) {
-            // rows start 16-byte aligned: four rows of 64 columns per store
-            // instruction, 16 bytes per lane
-            const int c4 = J0 + 4 * (lane & 15);
-            if (c4 < a.nb) {
-                for (int i = lane >> 4; i < 64; i += 4) {
-                    const int I = I0 + i;
-                    if (I >= a.nb) break;
-                    *reinterpret_cast<f32x4 *>(out + (size_t)I * a.nb + c4) = f32x4{ninf, ninf, ninf, ninf};
-                }
-            }
-        } else {
-            for (int i = 0; i < 64; ++i) {
-                const int I = I0 + i;
-                if (I >= a.nb) break;
-                if (J0 + lane < a.nb) out[(size_t)I * a.nb + J0 + lane] = ninf;
-            }
-        }
-        return;
-    }
+    if (J0 > I0 + 63) return;                   // wholly above the diagonal: not written
 
     const float *qb = a.qbar + ((size_t)b * a.hq + h) * a.nb * D + 4 * kh;
     const float *kb = a.kbar + ((size_t)b * a.hkv + g) * a.nb * D + 4 * kh;
@@ -382,7 +366,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int I = I0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
-                if (I < a.nb) out[(size_t)I * a.nb + J] = J <= I ? fmaf(acc[i][j][v], a.tau, lj) : ninf;
+                if (I < a.nb && J <= I) out[(size_t)I * a.nb + J] = fmaf(acc[i][j][v], a.tau, lj);
             }
     }
 }
@@ -402,7 +386,7 @@ hipError_t launch_score(const Shape &s, const float *qbar, const float *kbar, co
                         float *scores, hipStream_t st) {
     const int tiles = (s.nb + kTile - 1) / kTile;
     ScoreArgs a{qbar, kbar, lvn, scores, s.hq, s.hkv, s.nb, tiles, s.tau};
-    const dim3 grid(tiles * tiles, s.hq, s.batch);
+    const dim3 grid(tiles * (tiles + 1) / 2, s.hq, s.batch);
     if (s.d == 64) hipLaunchKernelGGL(score_kernel<64>, grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(score_kernel<128>, grid, dim3(256), 0, st, a);
     return hipGetLastError();

@@ -118,8 +118,8 @@ int stem_score_workspace_size(const stem_attn_desc *desc, size_t *bytes);
 
 /* OAM block scores (Stem article §一.3.2, §二.2.1):
  *   scores[b, h, I, J] = tau * <qbar[b,h,I], kbar[b,g(h),J]> + lvn[b,g(h),J]   for J <= I
- *   scores[b, h, I, J] = -inf                                                   for J >  I
- * scores: fp32 [batch, num_q_heads, Nb, Nb].  All arithmetic is fp32 with a
+ * scores: fp32 [batch, num_q_heads, Nb, Nb]; entries with J > I are not
+ * written (the selection never reads them).  All arithmetic is fp32 with a
  * fixed summation order, so repeated calls give identical bits.
  * workspace: device memory of at least stem_score_workspace_size() bytes. */
 int stem_score(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
@@ -127,7 +127,7 @@ int stem_score(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv
 
 /* SAM block scores: stem_score without the value term (the score-only
  * metric the setupai.cc summary, "Technical Deep Dive", contrasts OAM with):
- *   scores[b, h, I, J] = tau * <qbar[b,h,I], kbar[b,g(h),J]>   for J <= I, -inf above.
+ *   scores[b, h, I, J] = tau * <qbar[b,h,I], kbar[b,g(h),J]>   for J <= I (J > I not written).
  * Arguments, workspace and errors as stem_score; the lvn region of the
  * workspace is left unwritten. */
 int stem_score_sam(const stem_attn_desc *desc, const void *q, const stem_kv_desc *kv,
