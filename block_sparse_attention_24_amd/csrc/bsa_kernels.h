@@ -30,6 +30,7 @@
 //     straight into LDS; bsa_kernel (all other shapes) alternates MFMA and
 //     softmax phases between the two waves of a SIMD, with register-staged
 //     loads.  Each is described where it is defined.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -870,14 +871,21 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     float *part_ml = reinterpret_cast<float *>(smem + ML_OFF);
     float *half_max = reinterpret_cast<float *>(smem + HM_OFF);   // SKIP only
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    // Persistent workgroups: one per CU, each walking rows wg = blockIdx.x,
+    // blockIdx.x + gridDim.x, ... (row_body below), with a barrier between
+    // rows so that a row's loads into LDS never overwrite what the previous
+    // row still reads.
+    auto row_body = [&](const int wg) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));                          // derived per row, not held across rows
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g32 = lane >> 5, r32 = lane & 31;
     const int wq = wave & 3;                               // query group: rows 32 wq .. 32 wq + 31
     const int ks = wave >> 2;                              // key half: keys 64 ks .. 64 ks + 63 of each block
-
     // heaviest query blocks first; the heads of one KV group on one XCD
-    const int wg = blockIdx.x;
+    // (workgroup ids, and so the rows a persistent workgroup takes, go round-
+    // robin over the 8 XCDs)
     const int qidx = wg / a.hq, jh = wg % a.hq;
     const int I = a.nb - 1 - qidx / a.batch;
     const int b = qidx % a.batch;
@@ -1353,6 +1361,12 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     if (a.lse && g32 == 0)
         a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
     if (SKIP && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
+    };
+    const int rows = a.batch * a.hq * a.nb;
+    for (int wg = blockIdx.x; wg < rows; wg += gridDim.x) {
+        row_body(wg);
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1794,6 +1808,21 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
     if (a.lse && g32 == 0)
         a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
     if (SKIP && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
+}
+
+// Grid of the persistent attention kernels: one workgroup per compute unit
+// of the current device (they use all of a CU's LDS), at most `rows`.  The
+// CU count is asked once per device.
+__host__ inline unsigned persistent_grid(int rows) {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return (unsigned)(rows < n ? rows : n);
 }
 
 // Kernel arguments of one attention call (no online skip).
