@@ -1182,19 +1182,18 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             mc = (M - 8.0f) + ce;
             if constexpr (SKIP) mc = skip ? __builtin_huge_valf() : mc;   // dropped: P = 0
         }
-        SB();
-        sn[1] = mfma8(kb, qop(0), f32x16{}, 127);
-        SB();
-        dma_k(integral_constant<int, 1>{});
-        kb = kop(KRD, 1, 1);
+        // The softmax of block j runs on quads of scores (quad q: tile q >> 2,
+        // scores 4 (q & 3) .. 4 (q & 3) + 3) in three steps, the exp2 argument,
+        // the exp2, then the sums and the E4M3 pack, each one MFMA slot after
+        // the one before, so that no step waits on its predecessor's latency.
         float ls[4];
-        auto expq = [&](int t, int e0) {                  // P of 4 scores, into the partial sums
+        auto fq = [&](int q) {
 #pragma unroll
-            for (int e = e0; e < e0 + 4; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(sc[t][e], c, -mc));
-                sc[t][e] = pe;
-                ls[e & 3] = (t == 0 && e0 == 0) ? pe : ls[e & 3] + pe;
-            }
+            for (int e = 4 * (q & 3); e < 4 * (q & 3) + 4; ++e) sc[q >> 2][e] = fmaf(sc[q >> 2][e], c, -mc);
+        };
+        auto eq = [&](int q) {
+#pragma unroll
+            for (int e = 4 * (q & 3); e < 4 * (q & 3) + 4; ++e) sc[q >> 2][e] = __builtin_amdgcn_exp2f(sc[q >> 2][e]);
         };
         auto packq = [&](int w) {                          // 4 P of P word w as E4M3
             const f32x16 &src = sc[w >> 2];
@@ -1211,24 +1210,35 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
                 plo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(src[ee + 2] - h23[0], src[ee + 3] - h23[1], y, true);
             }
         };
+        auto aq = [&](int q) {                            // P into the partial sums, then packed
+#pragma unroll
+            for (int e = 4 * (q & 3); e < 4 * (q & 3) + 4; ++e) ls[e & 3] = q == 0 ? sc[0][e] : ls[e & 3] + sc[q >> 2][e];
+            packq(q);
+        };
         // one softmax slice per MFMA slot, skipped as a whole (one wave-uniform
         // branch) when no row of the wave keeps block j
         auto slice = [&](auto f) {
             if (soft) f();
         };
-        slice([&] { expq(0, 0); });
+        slice([&] { fq(0); });
+        SB();
+        sn[1] = mfma8(kb, qop(0), f32x16{}, 127);
+        SB();
+        dma_k(integral_constant<int, 1>{});
+        kb = kop(KRD, 1, 1);
+        slice([&] { fq(1); eq(0); });
         SB();
         sn[0] = mfma8(ka, qop(1), sn[0], 127);
         SB();
         dma_v(integral_constant<int, 0>{});
         i32x8 vb = PH == 1 ? i32x8{} : vop(VRD, 1);
-        slice([&] { expq(0, 4); packq(0); });
+        slice([&] { fq(2); eq(1); aq(0); });
         SB();
         sn[1] = mfma8(kb, qop(1), sn[1], 127);
         SB();
         kfirst = kop(KST + ((R + 2) % NST) * TILE, 0, 0);  // K(j+2): the first operand of S(j+2)
         dma_v(integral_constant<int, 1>{});
-        slice([&] { expq(0, 8); packq(1); });
+        slice([&] { fq(3); eq(2); aq(1); });
         // PV(j-1) (none in iteration 0)
         auto pv = [&](int dt, const i32x8 &vx) {
             if constexpr (PH != 1) o[dt] = mfma8(vx, pv_in, o[dt], psc_in);
@@ -1237,20 +1247,20 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         pv(0, va);
         SB();
         if constexpr (PH != 1) va = vop(VRD, 2);
-        slice([&] { expq(0, 12); packq(2); packq(3); });
+        slice([&] { fq(4); eq(3); aq(2); });
         SB();
         pv(1, vb);
         SB();
         if constexpr (PH != 1) vb = vop(VRD, 3);
-        slice([&] { expq(1, 0); });
+        slice([&] { fq(5); eq(4); aq(3); });
         SB();
         pv(2, va);
         SB();
-        slice([&] { expq(1, 4); packq(4); });
+        slice([&] { fq(6); fq(7); eq(5); aq(4); });
         SB();
         pv(3, vb);
         SB();
-        slice([&] { expq(1, 8); packq(5); });
+        slice([&] { eq(6); eq(7); aq(5); });
         if constexpr (SKIP) {
             // made here, each block, so that it holds no registers through the region
 #pragma unroll
@@ -1259,7 +1269,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         SB();
         if constexpr (PH != 1) lacc = mfma8(ones, pv_in, lacc, psc_in);
         SB();
-        slice([&] { expq(1, 12); packq(6); packq(7); });
+        slice([&] { aq(6); aq(7); });
         if (soft) {
             const int ice = (int)ce;
             l = fmaf(l, alpha, ldexpf((ls[0] + ls[1]) + (ls[2] + ls[3]), ice - 8));
