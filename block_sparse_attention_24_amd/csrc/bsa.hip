@@ -9,19 +9,19 @@ namespace {
 template <int DT, int D, int BLK>
 hipError_t launch_cfg(const BsaArgs &a, bool sparse, hipStream_t st) {
     using G = Geo<DT, D, BLK>;
-    const dim3 grid((unsigned)(a.batch * a.hq * a.nb));
+    const dim3 grid((unsigned)(a.batch * a.hq * a.nb));       // one workgroup per row
+    const dim3 pgrid(persistent_grid(a.batch * a.hq * a.nb));  // persistent: one workgroup per CU
     const bool paged = a.table != nullptr;
     if constexpr (DT == kFP8 && D == 128 && BLK == 128) {
-        const dim3 pgrid(persistent_grid(a.batch * a.hq * a.nb));   // one workgroup per CU
         if (sparse && paged) hipLaunchKernelGGL((bsa_fp8_kernel<true, true, false>), pgrid, dim3(fp8p::NT), 0, st, a);
         else if (sparse) hipLaunchKernelGGL((bsa_fp8_kernel<true, false, false>), pgrid, dim3(fp8p::NT), 0, st, a);
         else if (paged) hipLaunchKernelGGL((bsa_fp8_kernel<false, true, false>), pgrid, dim3(fp8p::NT), 0, st, a);
         else hipLaunchKernelGGL((bsa_fp8_kernel<false, false, false>), pgrid, dim3(fp8p::NT), 0, st, a);
     } else if constexpr (DT == kBF16 && D == 128 && BLK == 128) {
-        if (sparse && paged) hipLaunchKernelGGL((bsa_bf16_kernel<true, true, false>), grid, dim3(bf16p::NT), 0, st, a);
-        else if (sparse) hipLaunchKernelGGL((bsa_bf16_kernel<true, false, false>), grid, dim3(bf16p::NT), 0, st, a);
-        else if (paged) hipLaunchKernelGGL((bsa_bf16_kernel<false, true, false>), grid, dim3(bf16p::NT), 0, st, a);
-        else hipLaunchKernelGGL((bsa_bf16_kernel<false, false, false>), grid, dim3(bf16p::NT), 0, st, a);
+        if (sparse && paged) hipLaunchKernelGGL((bsa_bf16_kernel<true, true, false>), pgrid, dim3(bf16p::NT), 0, st, a);
+        else if (sparse) hipLaunchKernelGGL((bsa_bf16_kernel<true, false, false>), pgrid, dim3(bf16p::NT), 0, st, a);
+        else if (paged) hipLaunchKernelGGL((bsa_bf16_kernel<false, true, false>), pgrid, dim3(bf16p::NT), 0, st, a);
+        else hipLaunchKernelGGL((bsa_bf16_kernel<false, false, false>), pgrid, dim3(bf16p::NT), 0, st, a);
     } else {
         if (sparse && paged) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, true, true>), grid, dim3(G::NT), 0, st, a);
         else if (sparse) hipLaunchKernelGGL((bsa_kernel<DT, D, BLK, true, false>), grid, dim3(G::NT), 0, st, a);

@@ -859,6 +859,19 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned lds, unsigned vo
 }
 }  // namespace fp8p
 
+// Row taken by a persistent workgroup at step t, where r = blockIdx.x +
+// t gridDim.x.  Rows are numbered query block major (qidx = r / hq, heaviest
+// first) and head minor, so a grid that is a multiple of hq keeps each
+// workgroup on one head (and one KV group per XCD).  Odd steps take their
+// query blocks in reverse order, so that each workgroup's sum of row lengths
+// (causal: longest first) comes out about equal.
+__device__ __forceinline__ int persistent_row(const BsaArgs &a, int r, int t) {
+    const int per = (int)gridDim.x / a.hq;                 // query blocks per step
+    if ((t & 1) && per > 0 && (int)gridDim.x == per * a.hq && (t + 1) * per <= a.batch * a.nb)
+        return (t * per + (per - 1 - (int)blockIdx.x / a.hq)) * a.hq + r % a.hq;
+    return r;
+}
+
 template <bool SPARSE, bool PAGED, bool SKIP>
 __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     using namespace fp8p;
@@ -1373,8 +1386,8 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     if (SKIP && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
     };
     const int rows = a.batch * a.hq * a.nb;
-    for (int wg = blockIdx.x; wg < rows; wg += gridDim.x) {
-        row_body(wg);
+    for (int r = blockIdx.x, t = 0; r < rows; r += gridDim.x, ++t) {
+        row_body(persistent_row(a, r, t));
         __syncthreads();
     }
 }
@@ -1428,14 +1441,18 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
     float *part_ml = reinterpret_cast<float *>(smem + ML_OFF);
     float *half_max = reinterpret_cast<float *>(smem + HM_OFF);   // SKIP only
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    // Persistent workgroups, as in bsa_fp8_kernel: rows wg = blockIdx.x,
+    // blockIdx.x + gridDim.x, ..., with a barrier between rows.
+    auto row_body = [&](const int wg) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));                          // derived per row, not held across rows
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g32 = lane >> 5, r32 = lane & 31;
     const int wq = wave & 3;                               // query group: rows 32 wq .. 32 wq + 31
     const int ks = wave >> 2;                              // key half: keys 64 ks .. 64 ks + 63 of each block
 
     // heaviest query blocks first; the heads of one KV group on one XCD
-    const int wg = blockIdx.x;
     const int qidx = wg / a.hq, jh = wg % a.hq;
     const int I = a.nb - 1 - qidx / a.batch;
     const int b = qidx % a.batch;
@@ -1818,6 +1835,12 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
     if (a.lse && g32 == 0)
         a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
     if (SKIP && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
+    };
+    const int rows = a.batch * a.hq * a.nb;
+    for (int r = blockIdx.x, t = 0; r < rows; r += gridDim.x, ++t) {
+        row_body(persistent_row(a, r, t));
+        __syncthreads();
+    }
 }
 
 // Grid of the persistent attention kernels: one workgroup per compute unit

@@ -12,19 +12,18 @@ namespace {
 // The pipelined kernels with the online skip (d = 128, 128-token blocks).
 template <int DT>
 hipError_t launch_skip(const BsaArgs &a, bool sparse, hipStream_t st) {
-    const dim3 grid((unsigned)(a.batch * a.hq * a.nb));
+    const dim3 pgrid(persistent_grid(a.batch * a.hq * a.nb));  // persistent: one workgroup per CU
     const bool paged = a.table != nullptr;
     if constexpr (DT == kFP8) {
-        const dim3 pgrid(persistent_grid(a.batch * a.hq * a.nb));   // one workgroup per CU
         if (sparse && paged) hipLaunchKernelGGL((bsa_fp8_kernel<true, true, true>), pgrid, dim3(fp8p::NT), 0, st, a);
         else if (sparse) hipLaunchKernelGGL((bsa_fp8_kernel<true, false, true>), pgrid, dim3(fp8p::NT), 0, st, a);
         else if (paged) hipLaunchKernelGGL((bsa_fp8_kernel<false, true, true>), pgrid, dim3(fp8p::NT), 0, st, a);
         else hipLaunchKernelGGL((bsa_fp8_kernel<false, false, true>), pgrid, dim3(fp8p::NT), 0, st, a);
     } else {
-        if (sparse && paged) hipLaunchKernelGGL((bsa_bf16_kernel<true, true, true>), grid, dim3(bf16p::NT), 0, st, a);
-        else if (sparse) hipLaunchKernelGGL((bsa_bf16_kernel<true, false, true>), grid, dim3(bf16p::NT), 0, st, a);
-        else if (paged) hipLaunchKernelGGL((bsa_bf16_kernel<false, true, true>), grid, dim3(bf16p::NT), 0, st, a);
-        else hipLaunchKernelGGL((bsa_bf16_kernel<false, false, true>), grid, dim3(bf16p::NT), 0, st, a);
+        if (sparse && paged) hipLaunchKernelGGL((bsa_bf16_kernel<true, true, true>), pgrid, dim3(bf16p::NT), 0, st, a);
+        else if (sparse) hipLaunchKernelGGL((bsa_bf16_kernel<true, false, true>), pgrid, dim3(bf16p::NT), 0, st, a);
+        else if (paged) hipLaunchKernelGGL((bsa_bf16_kernel<false, true, true>), pgrid, dim3(bf16p::NT), 0, st, a);
+        else hipLaunchKernelGGL((bsa_bf16_kernel<false, false, true>), pgrid, dim3(bf16p::NT), 0, st, a);
     }
     return hipGetLastError();
 }
