@@ -806,8 +806,8 @@ constexpr int KST = 0, VST = NST * TILE;         // K stages, then V stages
 constexpr int LIST_OFF = 2 * NST * TILE;         // kept-block list (u16) after the stages
 constexpr int LIST = 4096 + 8;                   // up to 4096 kept blocks, plus 8 pad entries
 constexpr int WSUM_OFF = LIST_OFF + 2 * LIST;    // per-wave counts of the list scan
-constexpr int ML_OFF = WSUM_OFF + 4 * NW;        // (M, l, lq) of the second key half
-constexpr int HM_OFF = ML_OFF + 3 * 4 * 64 * 4;  // online skip: half-block maxima, [parity][wave][lane]
+constexpr int ML_OFF = WSUM_OFF + 4 * NW;        // (M, l, lq) of every wave, for the key-half merge
+constexpr int HM_OFF = ML_OFF + 3 * NW * 64 * 4; // online skip: half-block maxima, [parity][wave][lane]
 constexpr int SMEM = HM_OFF;
 constexpr int SMEM_SKIP = HM_OFF + 2 * NW * 64 * 4;
 static_assert(SMEM_SKIP <= 160 * 1024, "LDS of one CU");
@@ -859,6 +859,53 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned lds, unsigned vo
 }
 }  // namespace fp8p
 
+// Thread tid's 32-bit word of the mask row of attention row wg (rows numbered
+// as in the pipelined kernels): words 0 .. I/32 hold the blocks J <= I; the
+// other threads get 0.  Issued a row ahead by the persistent kernels.
+__device__ __forceinline__ uint32_t mask_word(const BsaArgs &a, int wg, int tid) {
+    const int qidx = wg / a.hq, jh = wg % a.hq;
+    const int I = a.nb - 1 - qidx / a.batch, b = qidx % a.batch;
+    const int h = (a.hq % 8 == 0) ? (jh % 8) * (a.hq / 8) + jh / 8 : jh;
+    return tid <= (I >> 5) ? a.mask[(((size_t)b * a.hq + h) * a.nb + I) * a.words + tid] : 0u;
+}
+
+// The kept-block list of row I from its mask words (thread tid holds word
+// tid, as mask_word gives it), in increasing J, into LDS; returns its length.
+// The words and their list offsets pass through wbuf (2 x 128 u32 of LDS);
+// then every thread places the kept blocks among 32 J at a time, so a dense
+// word costs one pass, not 32.  Up to 4096 blocks (128 words, two waves).
+template <int NW>
+__device__ __forceinline__ int build_list_words(int I, uint32_t w, uint16_t *list, uint32_t *wbuf, int *wave_sum,
+                                                int tid, int lane, int wave) {
+    const int nw = (I >> 5) + 1;                          // words holding J <= I
+    if (tid == nw - 1 && (I & 31) != 31) w &= (2u << (I & 31)) - 1u;
+    const int cnt = __popc(w);
+    int incl = cnt;                                       // inclusive scan in the wave
+    if (wave < 2) {                                       // words live in waves 0 and 1 only
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+    }
+    if (lane == 63) wave_sum[wave] = incl;
+    if (tid < nw) {
+        wbuf[tid] = w;
+        wbuf[128 + tid] = (uint32_t)(incl - cnt);         // offset within its wave
+    }
+    __syncthreads();
+    const int off1 = wave_sum[0];                         // kept blocks of words 0..63
+    const int n = off1 + wave_sum[1];
+    for (int k = tid; k < 32 * nw; k += NW * 64) {
+        const int x = k >> 5, bit = k & 31;
+        const uint32_t ww = wbuf[x];
+        if ((ww >> bit) & 1u)
+            list[(x >= 64 ? off1 : 0) + (int)wbuf[128 + x] + __popc(ww & ((1u << bit) - 1u))] = (uint16_t)k;
+    }
+    __syncthreads();
+    return n;
+}
+
 // Row taken by a persistent workgroup at step t, where r = blockIdx.x +
 // t gridDim.x.  Rows are numbered query block major (qidx = r / hq, heaviest
 // first) and head minor, so a grid that is a multiple of hq keeps each
@@ -888,7 +935,8 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     // blockIdx.x + gridDim.x, ... (row_body below), with a barrier between
     // rows so that a row's loads into LDS never overwrite what the previous
     // row still reads.
-    auto row_body = [&](const int wg) {
+    uint32_t wcur = 0, wnext = 0;                          // this row's and the next row's mask word
+    auto row_body = [&](const int wg, const int next) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));                          // derived per row, not held across rows
     const int lane = tid & 63;
@@ -909,7 +957,14 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     const int token = I * BLK + qrow;
     QFrag<kFP8, D> qf;                                     // in flight while the list is built
     load_q<kFP8, D>(qf, a.q + (((size_t)b * a.seq + token) * a.hq + h) * (size_t)D, g32);
-    const int n = build_block_list<NW, SPARSE>(a, b, h, I, list, wave_sum, tid, lane, wave);
+    int n = I + 1;
+    if constexpr (SPARSE) {
+        // the stages are free here: the previous row ended with every load done
+        n = build_list_words<NW>(I, wcur, list, reinterpret_cast<uint32_t *>(smem), wave_sum, tid, lane, wave);
+        // the next row's word, in flight through this row (issued after Q, so
+        // that the wait for Q below leaves it outstanding)
+        wnext = next >= 0 ? mask_word(a, next, tid) : 0u;
+    }
     if (n == 0) {
         if (ks == 0) write_empty_row<kFP8, D>(a, b, h, token, g32);
         if (SKIP && a.skipped && ks == 0 && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = 0;
@@ -1343,51 +1398,70 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     }
 
     // ---- merge the key halves, normalise, store -------------------------------
+    // The two waves of a query group each finalise two of the four d tiles
+    // (key half ks: tiles 2 ks, 2 ks + 1).  Each hands the other two tiles and
+    // its (M, l, lq) to its partner (wave ^ 4) through LDS.
     l = sum_xor32(l);                                      // exact sum of P: the LSE
     float lq = lacc[0];                                    // sum of the quantised P: O's denominator
     sync_vm<0, true>();                                    // every load into LDS is done: stages are free
-    float *po = reinterpret_cast<float *>(smem) + wq * 64 * (D / 2);
-    if (ks == 1) {
+    auto hand_over = [&](auto KSC) {
+        constexpr int K = decltype(KSC)::value;
+        float *pout = reinterpret_cast<float *>(smem) + wave * (32 * 64);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) po[(dt * 16 + e) * 64 + lane] = o[dt][e];
-        part_ml[(3 * wq) * 64 + lane] = M;
-        part_ml[(3 * wq + 1) * 64 + lane] = l;
-        part_ml[(3 * wq + 2) * 64 + lane] = lq;
-    }
+            for (int e = 0; e < 16; ++e) pout[(u * 16 + e) * 64 + lane] = o[2 * (1 - K) + u][e];
+    };
+    if (ks == 0) hand_over(integral_constant<int, 0>{});
+    else hand_over(integral_constant<int, 1>{});
+    part_ml[(3 * wave) * 64 + lane] = M;
+    part_ml[(3 * wave + 1) * 64 + lane] = l;
+    part_ml[(3 * wave + 2) * 64 + lane] = lq;
     __syncthreads();
-    if (ks == 1) return;
-    const float M1 = part_ml[(3 * wq) * 64 + lane];
-    const float l1 = part_ml[(3 * wq + 1) * 64 + lane];
-    const float lq1 = part_ml[(3 * wq + 2) * 64 + lane];
-    const float mm = fmaxf(M, M1);
-    const float a0 = __builtin_amdgcn_exp2f(M - mm), a1 = __builtin_amdgcn_exp2f(M1 - mm);
+    auto finish = [&](auto KSC) {
+        constexpr int K = decltype(KSC)::value;
+        const int pw = wave ^ 4;                           // the partner: the other key half
+        const float Mp = part_ml[(3 * pw) * 64 + lane];
+        const float lp = part_ml[(3 * pw + 1) * 64 + lane];
+        const float lqp = part_ml[(3 * pw + 2) * 64 + lane];
+        // key half 0 first, so that both waves form identical sums
+        const float M0 = K ? Mp : M, M1 = K ? M : Mp;
+        const float mm = fmaxf(M0, M1);
+        const float a0 = __builtin_amdgcn_exp2f(M0 - mm), a1 = __builtin_amdgcn_exp2f(M1 - mm);
+        const float lt = fmaf(K ? lp : l, a0, (K ? l : lp) * a1);
+        const float lqt = fmaf(K ? lqp : lq, a0, (K ? lq : lqp) * a1);
+        const float as = K ? a1 : a0, ap = K ? a0 : a1;   // own and partner's factor
+        const float inv = lqt > 0.0f ? a.o_scale / lqt : 0.0f;
+        const float *pin = reinterpret_cast<const float *>(smem) + pw * (32 * 64);
+        const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+        for (int u = 0; u < 2; ++u) {
+            const int dt = 2 * K + u;
+            f32x16 x;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] = o[dt][e] * a0 + po[(dt * 16 + e) * 64 + lane] * a1;
-    l = l * a0 + l1 * a1;
-    lq = lq * a0 + lq1 * a1;
-    const float inv = lq > 0.0f ? a.o_scale / lq : 0.0f;
-    const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
+            for (int e = 0; e < 16; ++e) x[e] = fmaf(o[2 * K + u][e], as, pin[(u * 16 + e) * 64 + lane] * ap) * inv;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = 32 * dt + 8 * i + 4 * g32;
-            u32x2 u;
-            u.x = f32_to_bf16_bits(o[dt][4 * i] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 1] * inv) << 16);
-            u.y = f32_to_bf16_bits(o[dt][4 * i + 2] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 3] * inv) << 16);
-            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = u;
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * dt + 8 * i + 4 * g32;
+                u32x2 v2;
+                v2.x = f32_to_bf16_bits(x[4 * i]) | (f32_to_bf16_bits(x[4 * i + 1]) << 16);
+                v2.y = f32_to_bf16_bits(x[4 * i + 2]) | (f32_to_bf16_bits(x[4 * i + 3]) << 16);
+                *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = v2;
+            }
         }
-    if (a.lse && g32 == 0)
-        a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
-    if (SKIP && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
+        if (K == 0 && a.lse && g32 == 0)
+            a.lse[((size_t)b * a.hq + h) * a.seq + token] = lt > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(lt)) : ninf;
+        if (SKIP && K == 0 && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
+    };
+    if (ks == 0) finish(integral_constant<int, 0>{});
+    else finish(integral_constant<int, 1>{});
     };
     const int rows = a.batch * a.hq * a.nb;
+    if (SPARSE && (int)blockIdx.x < rows) wcur = mask_word(a, persistent_row(a, blockIdx.x, 0), threadIdx.x);
     for (int r = blockIdx.x, t = 0; r < rows; r += gridDim.x, ++t) {
-        row_body(persistent_row(a, r, t));
+        const int rn = r + (int)gridDim.x;
+        row_body(persistent_row(a, r, t), rn < rows ? persistent_row(a, rn, t + 1) : -1);
+        wcur = wnext;
         __syncthreads();
     }
 }
@@ -1416,8 +1490,8 @@ constexpr int KST = 0, VST = 2 * TILE;           // two K stages, then two V sta
 constexpr int LIST_OFF = 4 * TILE;               // kept-block list (u16) after the stages
 constexpr int LIST = 4096 + 8;                   // up to 4096 kept blocks, plus 8 pad entries
 constexpr int WSUM_OFF = LIST_OFF + 2 * LIST;    // per-wave counts of the list scan
-constexpr int ML_OFF = WSUM_OFF + 4 * NW;        // (M, l) of the second key half
-constexpr int HM_OFF = ML_OFF + 2 * 4 * 64 * 4;  // online skip: half-block maxima, [parity][wave][lane]
+constexpr int ML_OFF = WSUM_OFF + 4 * NW;        // (M, l) of every wave, for the key-half merge
+constexpr int HM_OFF = ML_OFF + 2 * NW * 64 * 4; // online skip: half-block maxima, [parity][wave][lane]
 constexpr int SMEM = HM_OFF;
 constexpr int SMEM_SKIP = HM_OFF + 2 * NW * 64 * 4;
 constexpr float THRESH = 8.0f;                   // lazy rescale: P stays below 2^THRESH
@@ -1443,7 +1517,8 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
 
     // Persistent workgroups, as in bsa_fp8_kernel: rows wg = blockIdx.x,
     // blockIdx.x + gridDim.x, ..., with a barrier between rows.
-    auto row_body = [&](const int wg) {
+    uint32_t wcur = 0, wnext = 0;                          // this row's and the next row's mask word
+    auto row_body = [&](const int wg, const int next) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));                          // derived per row, not held across rows
     const int lane = tid & 63;
@@ -1463,7 +1538,13 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
     const int token = I * BLK + qrow;
     QFrag<kBF16, D> qf;                                    // in flight while the list is built
     load_q<kBF16, D>(qf, a.q + (((size_t)b * a.seq + token) * a.hq + h) * (size_t)ROWB, g32);
-    const int n = build_block_list<NW, SPARSE>(a, b, h, I, list, wave_sum, tid, lane, wave);
+    int n = I + 1;
+    if constexpr (SPARSE) {
+        // as in bsa_fp8_kernel: the stages are free here, and the next row's
+        // word is issued after Q
+        n = build_list_words<NW>(I, wcur, list, reinterpret_cast<uint32_t *>(smem), wave_sum, tid, lane, wave);
+        wnext = next >= 0 ? mask_word(a, next, tid) : 0u;
+    }
     if (n == 0) {
         if (ks == 0) write_empty_row<kBF16, D>(a, b, h, token, g32);
         if (SKIP && a.skipped && ks == 0 && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = 0;
@@ -1798,47 +1879,63 @@ __global__ __launch_bounds__(512, 1) void bsa_bf16_kernel(BsaArgs a) {
     }
 
     // ---- merge the key halves, normalise, store -------------------------------
+    // As in bsa_fp8_kernel: each wave of a query group finalises two of the
+    // four d tiles and hands the other two, with its (M, l), to wave ^ 4.
     l = sum_xor32(l);
     sync_vm<0, true>();                                    // every load into LDS is done: stages are free
-    float *po = reinterpret_cast<float *>(smem) + wq * 64 * (D / 2);
-    if (ks == 1) {
+    auto hand_over = [&](auto KSC) {
+        constexpr int K = decltype(KSC)::value;
+        float *pout = reinterpret_cast<float *>(smem) + wave * (32 * 64);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) po[(dt * 16 + e) * 64 + lane] = o[dt][e];
-        part_ml[(2 * wq) * 64 + lane] = M;
-        part_ml[(2 * wq + 1) * 64 + lane] = l;
-    }
+            for (int e = 0; e < 16; ++e) pout[(u * 16 + e) * 64 + lane] = o[2 * (1 - K) + u][e];
+    };
+    if (ks == 0) hand_over(integral_constant<int, 0>{});
+    else hand_over(integral_constant<int, 1>{});
+    part_ml[(2 * wave) * 64 + lane] = M;
+    part_ml[(2 * wave + 1) * 64 + lane] = l;
     __syncthreads();
-    if (ks == 1) return;
-    const float M1 = part_ml[(2 * wq) * 64 + lane];
-    const float l1 = part_ml[(2 * wq + 1) * 64 + lane];
-    const float mm = fmaxf(M, M1);
-    const float a0 = __builtin_amdgcn_exp2f(M - mm), a1 = __builtin_amdgcn_exp2f(M1 - mm);
+    auto finish = [&](auto KSC) {
+        constexpr int K = decltype(KSC)::value;
+        const int pw = wave ^ 4;                           // the partner: the other key half
+        const float Mp = part_ml[(2 * pw) * 64 + lane];
+        const float lp = part_ml[(2 * pw + 1) * 64 + lane];
+        const float M0 = K ? Mp : M, M1 = K ? M : Mp;     // key half 0 first: identical sums
+        const float mm = fmaxf(M0, M1);
+        const float a0 = __builtin_amdgcn_exp2f(M0 - mm), a1 = __builtin_amdgcn_exp2f(M1 - mm);
+        const float lt = fmaf(K ? lp : l, a0, (K ? l : lp) * a1);
+        const float as = K ? a1 : a0, ap = K ? a0 : a1;   // own and partner's factor
+        const float inv = lt > 0.0f ? a.o_scale / lt : 0.0f;
+        const float *pin = reinterpret_cast<const float *>(smem) + pw * (32 * 64);
+        const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+        for (int u = 0; u < 2; ++u) {
+            f32x16 x;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] = o[dt][e] * a0 + po[(dt * 16 + e) * 64 + lane] * a1;
-    l = l * a0 + l1 * a1;
-    const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
-    const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
+            for (int e = 0; e < 16; ++e) x[e] = fmaf(o[2 * K + u][e], as, pin[(u * 16 + e) * 64 + lane] * ap) * inv;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = 32 * dt + 8 * i + 4 * g32;
-            u32x2 u;
-            u.x = f32_to_bf16_bits(o[dt][4 * i] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 1] * inv) << 16);
-            u.y = f32_to_bf16_bits(o[dt][4 * i + 2] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 3] * inv) << 16);
-            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = u;
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * (2 * K + u) + 8 * i + 4 * g32;
+                u32x2 v2;
+                v2.x = f32_to_bf16_bits(x[4 * i]) | (f32_to_bf16_bits(x[4 * i + 1]) << 16);
+                v2.y = f32_to_bf16_bits(x[4 * i + 2]) | (f32_to_bf16_bits(x[4 * i + 3]) << 16);
+                *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = v2;
+            }
         }
-    if (a.lse && g32 == 0)
-        a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
-    if (SKIP && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
+        if (K == 0 && a.lse && g32 == 0)
+            a.lse[((size_t)b * a.hq + h) * a.seq + token] = lt > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(lt)) : ninf;
+        if (SKIP && K == 0 && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
+    };
+    if (ks == 0) finish(integral_constant<int, 0>{});
+    else finish(integral_constant<int, 1>{});
     };
     const int rows = a.batch * a.hq * a.nb;
+    if (SPARSE && (int)blockIdx.x < rows) wcur = mask_word(a, persistent_row(a, blockIdx.x, 0), threadIdx.x);
     for (int r = blockIdx.x, t = 0; r < rows; r += gridDim.x, ++t) {
-        row_body(persistent_row(a, r, t));
+        const int rn = r + (int)gridDim.x;
+        row_body(persistent_row(a, r, t), rn < rows ? persistent_row(a, rn, t + 1) : -1);
+        wcur = wnext;
         __syncthreads();
     }
 }
