@@ -163,6 +163,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
     return max(r[0], r[1]);
 }
 
+// Sum of x over the wave, in every lane (the pairing of wave_min_u32).
+__device__ __forceinline__ int wave_sum_i32(int x) {
+    x += (int)dpp_u32<0xB1>((uint32_t)x);
+    x += (int)dpp_u32<0x4E>((uint32_t)x);
+    x += (int)dpp_u32<0x141>((uint32_t)x);
+    x += (int)dpp_u32<0x140>((uint32_t)x);
+    auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = (int)(r[0] + r[1]);
+    r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return (int)(r[0] + r[1]);
+}
+
 // Number of set bits of `m` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));

@@ -6,9 +6,12 @@
 // kernel from the plan's threshold grant (an O(1) integer computation).  The
 // sink J=0 and the diagonal J=I are kept; the best k_I - |{0,I}| candidates
 // J in [1, I-1] are found by a bitwise search for the k-th largest
-// order-preserving 32-bit key (scores held in registers, counted with wave
-// ballots), then ties at the threshold go to the smallest J by a prefix count
-// over the lanes in J order.  Output: the packed mask row (two 32-bit words
+// order-preserving 32-bit key (scores held in registers), then ties at the
+// threshold go to the smallest J by a prefix count over the lanes in J order.
+// The search counts on the VALU (per-lane counts, one wave sum per bit) while
+// the bucket of keys that share the threshold's decided bits holds more than
+// 64 keys; then that bucket is gathered into one key per lane and each
+// further bit costs one ballot.  Output: the packed mask row (two 32-bit words
 // per 64-lane chunk straight from a ballot) and, optionally, the kept list.
 #include "device_common.h"
 #include "stem_internal.h"
@@ -27,8 +30,115 @@ struct SelectArgs {
     TpdPlan plan;
 };
 
+// One row, its candidates in the first NCH chunks of key[] (chunks from
+// ceil(I/64) on hold only key 0).  Every chunk loop has a compile-time trip
+// count: no per-chunk branch.
+template <int NCH, int MAXC>
+__device__ __forceinline__ void select_row(const SelectArgs &a, const uint32_t (&key)[MAXC], long long row, int I,
+                                           int k_row, int want, int ncand, uint32_t *buf, int lane) {
+    // Threshold key t: the want-th largest key, by a bitwise search from the
+    // highest bit on which the row's candidate keys differ (the bits above it
+    // are common to all of them, so to t as well).  Invalid lanes hold key 0,
+    // which no trial value (it has a bit set) counts.
+    uint32_t t = 0u;
+    int need_eq = 0;                           // keys == t still to keep, smallest J first
+    const bool all = want >= ncand;
+    if (want > 0 && !all) {
+        uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int j = c * 64 + lane;
+            if (j >= 1 && j < I) {
+                kmin = min(kmin, key[c]);
+                kmax = max(kmax, key[c]);
+            }
+        }
+        int bit;
+        t = key_prefix(wave_min_u32(kmin), wave_max_u32(kmax), bit);
+        // The bucket: the keys whose bits above `bit` equal t's; `above` keys
+        // lie above it.  A trial value t | 2^bit is reached by the keys above
+        // the bucket and the bucket's keys with that bit set.
+        int above = 0, size = ncand;
+        bool found = false;
+        for (; bit >= 0 && size > 64; --bit) {
+            const uint32_t cand = t | (1u << bit);
+            int cl = 0;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) cl += key[c] >= cand ? 1 : 0;
+            const int cnt = __builtin_amdgcn_readfirstlane(wave_sum_i32(cl));
+            if (cnt >= want) {
+                t = cand;
+                size = cnt - above;
+            } else {
+                size -= cnt - above;
+                above = cnt;
+            }
+            // Exactly `want` keys are >= cand: they are the kept set whatever
+            // the lower bits hold, and with t = cand the rule below keeps
+            // every key > t and every key == t, i.e. exactly them.
+            if (cnt == want) {
+                found = true;
+                break;
+            }
+        }
+        if (!found && bit >= 0) {
+            // gather the bucket (at most 64 keys) into one key per lane, through LDS
+            const uint32_t hi = bit >= 31 ? 0u : ~0u << (bit + 1);
+            int run = 0;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int j = c * 64 + lane;
+                const bool in = j >= 1 && j < I && ((key[c] ^ t) & hi) == 0u;
+                const uint64_t m = ballot64(in);
+                if (in) buf[run + lanes_below(m)] = key[c];
+                run += __popcll(m);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const uint32_t kb = lane < run ? buf[lane] : 0u;
+            for (; bit >= 0; --bit) {
+                const uint32_t cand = t | (1u << bit);
+                const int cnt = above + __popcll(ballot64(kb >= cand));
+                if (cnt >= want) t = cand;
+                if (cnt == want) break;
+            }
+        }
+        int gt = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) gt += __popcll(ballot64(key[c] > t));
+        need_eq = want - gt;
+    }
+
+    uint32_t *mrow = a.mask + row * a.words;
+    int32_t *lrow = a.list ? a.list + row * a.list_stride : nullptr;
+    int run_eq = 0, run_keep = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int j = c * 64 + lane;
+        const bool valid = j >= 1 && j < I;
+        bool keep = false;
+        if (all) {                              // uniform branches: ballots stay wave-wide
+            keep = valid && want > 0;
+        } else if (want > 0) {
+            const bool eq = valid && key[c] == t;
+            const uint64_t eqm = ballot64(eq);
+            keep = valid && (key[c] > t || (eq && run_eq + lanes_below(eqm) < need_eq));
+            run_eq += __popcll(eqm);
+        }
+        keep = keep || j == 0 || j == I;
+        const uint64_t km = ballot64(keep);
+        if (lane < 2 && 2 * c + lane < a.words)
+            mrow[2 * c + lane] = lane == 0 ? (uint32_t)km : (uint32_t)(km >> 32);
+        const int pos = run_keep + lanes_below(km);
+        if (lrow && keep && pos < a.list_stride) lrow[pos] = j;
+        run_keep += __popcll(km);
+    }
+    for (int wd = 2 * NCH + lane; wd < a.words; wd += 64) mrow[wd] = 0u;   // J > I
+    if (a.count && lane == 0) a.count[row] = k_row;
+}
+
 template <int MAXC>
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+    __shared__ uint32_t gather[4][64];          // per wave: the bucket gathered for the last bits
     const int lane = threadIdx.x & 63;
     const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= a.rows) return;                  // whole wave exits together
@@ -37,7 +147,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     const int forced = I == 0 ? 1 : 2;
     const int want = k_row - forced;            // candidates to keep
     const int ncand = I > 1 ? I - 1 : 0;        // J in [1, I-1]
-    const int nch = (I + 63) >> 6;              // chunks holding J < I
+    const int nch = (I >> 6) + 1;               // chunks holding J <= I
     const float *srow = a.scores + row * a.nb;
 
     uint32_t key[MAXC];
@@ -49,72 +159,18 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
             if (j >= 1 && j < I) key[c] = order_key(srow[j]);
         }
     }
-
-    // Threshold key t: the want-th largest key, by a bitwise search from the
-    // highest bit on which the row's candidate keys differ (the bits above it
-    // are common to all of them, so to t as well).
-    uint32_t t = 0u;
-    int need_eq = 0;                           // keys == t still to keep, smallest J first
-    const bool all = want >= ncand;
-    if (want > 0 && !all) {
-        uint32_t kmin = ~0u, kmax = 0u;
-#pragma unroll
-        for (int c = 0; c < MAXC; ++c) {
-            const int j = c * 64 + lane;
-            if (c < nch && j >= 1 && j < I) {
-                kmin = min(kmin, key[c]);
-                kmax = max(kmax, key[c]);
-            }
-        }
-        int top;
-        t = key_prefix(wave_min_u32(kmin), wave_max_u32(kmax), top);
-        for (int bit = top; bit >= 0; --bit) {
-            const uint32_t cand = t | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int c = 0; c < MAXC; ++c)
-                if (c < nch) cnt += __popcll(ballot64(key[c] >= cand));
-            if (cnt >= want) t = cand;
-            // Exactly `want` keys are >= cand: they are the kept set whatever
-            // the lower bits hold, and with t = cand the rule below keeps
-            // every key > t and every key == t, i.e. exactly them.
-            if (cnt == want) break;
-        }
-        int gt = 0;
-#pragma unroll
-        for (int c = 0; c < MAXC; ++c)
-            if (c < nch) gt += __popcll(ballot64(key[c] > t));
-        need_eq = want - gt;
-    }
-
-    const int chunks_row = (a.nb + 63) >> 6;
-    uint32_t *mrow = a.mask + row * a.words;
-    int32_t *lrow = a.list ? a.list + row * a.list_stride : nullptr;
-    int run_eq = 0, run_keep = 0;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        if (c < chunks_row) {                   // uniform; keeps the loop fully unrolled
-            const int j = c * 64 + lane;
-            const bool valid = j >= 1 && j < I;
-            bool keep = false;
-            if (all) {                          // uniform branches: ballots stay wave-wide
-                keep = valid && want > 0;
-            } else if (want > 0) {
-                const bool eq = valid && key[c] == t;
-                const uint64_t eqm = ballot64(eq);
-                keep = valid && (key[c] > t || (eq && run_eq + lanes_below(eqm) < need_eq));
-                run_eq += __popcll(eqm);
-            }
-            keep = keep || j == 0 || j == I;
-            const uint64_t km = ballot64(keep);
-            if (lane < 2 && 2 * c + lane < a.words)
-                mrow[2 * c + lane] = lane == 0 ? (uint32_t)km : (uint32_t)(km >> 32);
-            const int pos = run_keep + lanes_below(km);
-            if (lrow && keep && pos < a.list_stride) lrow[pos] = j;
-            run_keep += __popcll(km);
-        }
-    }
-    if (a.count && lane == 0) a.count[row] = k_row;
+    uint32_t *buf = gather[threadIdx.x >> 6];
+    // the smallest compiled chunk count that covers the row (uniform branches)
+    if (nch <= 1) select_row<1>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else if (nch <= 2) select_row<(MAXC < 2 ? MAXC : 2)>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else if (nch <= 4) select_row<(MAXC < 4 ? MAXC : 4)>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else if (nch <= 8) select_row<(MAXC < 8 ? MAXC : 8)>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else if (nch <= 12) select_row<(MAXC < 12 ? MAXC : 12)>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else if (nch <= 16) select_row<(MAXC < 16 ? MAXC : 16)>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else if (nch <= 24) select_row<(MAXC < 24 ? MAXC : 24)>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else if (nch <= 32) select_row<(MAXC < 32 ? MAXC : 32)>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else if (nch <= 48) select_row<(MAXC < 48 ? MAXC : 48)>(a, key, row, I, k_row, want, ncand, buf, lane);
+    else select_row<MAXC>(a, key, row, I, k_row, want, ncand, buf, lane);
 }
 
 template <int MAXC>
