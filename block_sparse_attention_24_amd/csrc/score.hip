@@ -3,8 +3,9 @@
 // block score, with no softmax, no gather and no token-level intermediate).
 //
 // Kernels:
-//   pool_kernel         one HBM pass over Q, K or V: per block the mean of the
-//                       rows, or ln of the Frobenius norm of the V rows.
+//   pool_kernel         one HBM pass over Q, K and V (one launch): per block
+//                       the mean of the rows, or ln of the Frobenius norm of
+//                       the V rows.
 //   cache_write_kernel  the same block reductions fused into writing a
 //                       prefill's K and V into the (FP8, paged) cache: one pass
 //                       over the new tokens stores them and pools them.
@@ -112,12 +113,12 @@ __device__ __forceinline__ bool combine_row_groups(float *acc, float *part) {
     return true;
 }
 
-// Thread = one 16-byte column chunk of a token row in one row group.
+// Thread = one 16-byte column chunk of a token row in one row group; bx is
+// the workgroup's column group within its tensor.
 template <int ES, int MODE>
-__global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
+__device__ __forceinline__ void pool_body(const PoolArgs &a, int bx, float *part) {
     constexpr int EPC = 16 / ES;              // elements per chunk
-    __shared__ float part[(kRowGroups - 1) * EPC * kPoolChunks];
-    const int chunk = blockIdx.x * kPoolChunks + threadIdx.x % kPoolChunks;
+    const int chunk = bx * kPoolChunks + threadIdx.x % kPoolChunks;
     const int group = threadIdx.x / kPoolChunks;
     const int blk_j = blockIdx.y;
     const int b = blockIdx.z;
@@ -142,6 +143,23 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
     }
     if (combine_row_groups<EPC>(acc, part))
         pool_store<EPC, MODE>(acc, active, chunk, a.out, b, a.heads, a.nb, a.d, blk_j, a.blk, a.scale);
+}
+
+// Q, K and V pooled in one launch: column groups [0, g0) are Q's (means),
+// [g0, g1) K's (means), [g1, gridDim.x) V's (log-norms); n tensors are set
+// (Q alone when the keys' representations come from elsewhere, no V for SAM).
+struct PoolSet {
+    PoolArgs t[3];
+    int g0, g1;
+};
+
+template <int ES>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolSet p) {
+    __shared__ float part[(kRowGroups - 1) * (16 / ES) * kPoolChunks];
+    const int x = blockIdx.x;
+    if (x < p.g0) pool_body<ES, 0>(p.t[0], x, part);
+    else if (x < p.g1) pool_body<ES, 0>(p.t[1], x - p.g0, part);
+    else pool_body<ES, 1>(p.t[2], x - p.g1, part);
 }
 
 // ---------------------------------------------------------------------------
@@ -233,8 +251,8 @@ __global__ __launch_bounds__(kPoolThreads) void cache_write_kernel(CacheArgs a) 
 }
 
 template <int ES>
-hipError_t pool_one(const Shape &s, const void *base, const int32_t *table, int page_log2,
-                    int pages_per_seq, int heads, float scale, float *out, int mode, hipStream_t st) {
+PoolArgs pool_args(const Shape &s, const void *base, const int32_t *table, int page_log2, int pages_per_seq,
+                   int heads, float scale, float *out) {
     PoolArgs a{};
     a.base = static_cast<const char *>(base);
     a.out = out;
@@ -248,20 +266,27 @@ hipError_t pool_one(const Shape &s, const void *base, const int32_t *table, int 
     a.nb = s.nb;
     a.chunks_per_row = heads * s.d * ES / 16;
     a.scale = scale;
-    dim3 grid((a.chunks_per_row + kPoolChunks - 1) / kPoolChunks, s.nb, s.batch);
-    if (mode == 0) hipLaunchKernelGGL((pool_kernel<ES, 0>), grid, dim3(kPoolThreads), 0, st, a);
-    else hipLaunchKernelGGL((pool_kernel<ES, 1>), grid, dim3(kPoolThreads), 0, st, a);
-    return hipGetLastError();
+    return a;
 }
 
 template <int ES>
 hipError_t pool_all(const Shape &s, const void *q, const KvView *kv, float *qbar, float *kbar,
                     float *lvn, hipStream_t st) {
-    hipError_t e = pool_one<ES>(s, q, nullptr, 0, 0, s.hq, s.q_scale, qbar, 0, st);
-    if (e != hipSuccess || !kv) return e;
-    e = pool_one<ES>(s, kv->k, kv->table, kv->page_log2, kv->pages_per_seq, s.hkv, s.k_scale, kbar, 0, st);
-    if (e != hipSuccess || !lvn) return e;
-    return pool_one<ES>(s, kv->v, kv->table, kv->page_log2, kv->pages_per_seq, s.hkv, s.v_scale, lvn, 1, st);
+    PoolSet p{};
+    auto groups = [](const PoolArgs &a) { return (a.chunks_per_row + kPoolChunks - 1) / kPoolChunks; };
+    p.t[0] = pool_args<ES>(s, q, nullptr, 0, 0, s.hq, s.q_scale, qbar);
+    p.g0 = p.g1 = groups(p.t[0]);
+    int gx = p.g0;
+    if (kv) {
+        p.t[1] = pool_args<ES>(s, kv->k, kv->table, kv->page_log2, kv->pages_per_seq, s.hkv, s.k_scale, kbar);
+        p.g1 = gx = p.g0 + groups(p.t[1]);
+        if (lvn) {
+            p.t[2] = pool_args<ES>(s, kv->v, kv->table, kv->page_log2, kv->pages_per_seq, s.hkv, s.v_scale, lvn);
+            gx += groups(p.t[2]);
+        }
+    }
+    hipLaunchKernelGGL((pool_kernel<ES>), dim3(gx, s.nb, s.batch), dim3(kPoolThreads), 0, st, p);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

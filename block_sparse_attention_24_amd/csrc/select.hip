@@ -30,16 +30,25 @@ struct SelectArgs {
     TpdPlan plan;
 };
 
-// One row, its candidates in the first NCH chunks of key[] (chunks from
-// ceil(I/64) on hold only key 0).  Every chunk loop has a compile-time trip
-// count: no per-chunk branch.
-template <int NCH, int MAXC>
-__device__ __forceinline__ void select_row(const SelectArgs &a, const uint32_t (&key)[MAXC], long long row, int I,
-                                           int k_row, int want, int ncand, uint32_t *buf, int lane) {
+// One row, its candidates in the first NCH chunks of 64 J (chunks from
+// ceil(I/64) on hold only invalid J).  Every chunk loop has a compile-time
+// trip count and no branch: invalid J read a clamped, in-row address and get
+// key 0, which no trial value (it has a bit set) counts.
+template <int NCH>
+__device__ __forceinline__ void select_row(const SelectArgs &a, long long row, int I, int k_row, int want,
+                                           int ncand, uint32_t *buf, int lane) {
+    const float *srow = a.scores + row * a.nb;
+    uint32_t key[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int j = c * 64 + lane;
+        const float x = srow[min(j, I)];
+        key[c] = (j >= 1 && j < I) ? order_key(x) : 0u;
+    }
+
     // Threshold key t: the want-th largest key, by a bitwise search from the
     // highest bit on which the row's candidate keys differ (the bits above it
-    // are common to all of them, so to t as well).  Invalid lanes hold key 0,
-    // which no trial value (it has a bit set) counts.
+    // are common to all of them, so to t as well).
     uint32_t t = 0u;
     int need_eq = 0;                           // keys == t still to keep, smallest J first
     const bool all = want >= ncand;
@@ -48,10 +57,8 @@ __device__ __forceinline__ void select_row(const SelectArgs &a, const uint32_t (
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int j = c * 64 + lane;
-            if (j >= 1 && j < I) {
-                kmin = min(kmin, key[c]);
-                kmax = max(kmax, key[c]);
-            }
+            kmin = min(kmin, (j >= 1 && j < I) ? key[c] : ~0u);
+            kmax = max(kmax, key[c]);          // invalid J: 0, and some J is valid here
         }
         int bit;
         t = key_prefix(wave_min_u32(kmin), wave_max_u32(kmax), bit);
@@ -108,8 +115,13 @@ __device__ __forceinline__ void select_row(const SelectArgs &a, const uint32_t (
         need_eq = want - gt;
     }
 
-    uint32_t *mrow = a.mask + row * a.words;
+    // The kept set, chunk by chunk in J order; lane w collects mask words w,
+    // w + 64, ... (two words per chunk).
     int32_t *lrow = a.list ? a.list + row * a.list_stride : nullptr;
+    constexpr int MW = (2 * NCH + 63) / 64;
+    uint32_t mword[MW];
+#pragma unroll
+    for (int q = 0; q < MW; ++q) mword[q] = 0u;
     int run_eq = 0, run_keep = 0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -126,11 +138,18 @@ __device__ __forceinline__ void select_row(const SelectArgs &a, const uint32_t (
         }
         keep = keep || j == 0 || j == I;
         const uint64_t km = ballot64(keep);
-        if (lane < 2 && 2 * c + lane < a.words)
-            mrow[2 * c + lane] = lane == 0 ? (uint32_t)km : (uint32_t)(km >> 32);
-        const int pos = run_keep + lanes_below(km);
-        if (lrow && keep && pos < a.list_stride) lrow[pos] = j;
-        run_keep += __popcll(km);
+        if ((lane >> 1) == (c & 31)) mword[c >> 5] = (lane & 1) ? (uint32_t)(km >> 32) : (uint32_t)km;
+        if (lrow) {
+            const int pos = run_keep + lanes_below(km);
+            if (keep && pos < a.list_stride) lrow[pos] = j;
+            run_keep += __popcll(km);
+        }
+    }
+    uint32_t *mrow = a.mask + row * a.words;
+#pragma unroll
+    for (int q = 0; q < MW; ++q) {
+        const int wd = 64 * q + lane;
+        if (wd < 2 * NCH && wd < a.words) mrow[wd] = mword[q];
     }
     for (int wd = 2 * NCH + lane; wd < a.words; wd += 64) mrow[wd] = 0u;   // J > I
     if (a.count && lane == 0) a.count[row] = k_row;
@@ -148,29 +167,20 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     const int want = k_row - forced;            // candidates to keep
     const int ncand = I > 1 ? I - 1 : 0;        // J in [1, I-1]
     const int nch = (I >> 6) + 1;               // chunks holding J <= I
-    const float *srow = a.scores + row * a.nb;
-
-    uint32_t key[MAXC];
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        key[c] = 0u;
-        if (c < nch) {
-            const int j = c * 64 + lane;
-            if (j >= 1 && j < I) key[c] = order_key(srow[j]);
-        }
-    }
     uint32_t *buf = gather[threadIdx.x >> 6];
     // the smallest compiled chunk count that covers the row (uniform branches)
-    if (nch <= 1) select_row<1>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else if (nch <= 2) select_row<(MAXC < 2 ? MAXC : 2)>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else if (nch <= 4) select_row<(MAXC < 4 ? MAXC : 4)>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else if (nch <= 8) select_row<(MAXC < 8 ? MAXC : 8)>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else if (nch <= 12) select_row<(MAXC < 12 ? MAXC : 12)>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else if (nch <= 16) select_row<(MAXC < 16 ? MAXC : 16)>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else if (nch <= 24) select_row<(MAXC < 24 ? MAXC : 24)>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else if (nch <= 32) select_row<(MAXC < 32 ? MAXC : 32)>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else if (nch <= 48) select_row<(MAXC < 48 ? MAXC : 48)>(a, key, row, I, k_row, want, ncand, buf, lane);
-    else select_row<MAXC>(a, key, row, I, k_row, want, ncand, buf, lane);
+#define SEL(N) select_row<(MAXC < N ? MAXC : N)>(a, row, I, k_row, want, ncand, buf, lane)
+    if (nch <= 1) SEL(1);
+    else if (nch <= 2) SEL(2);
+    else if (nch <= 4) SEL(4);
+    else if (nch <= 8) SEL(8);
+    else if (nch <= 12) SEL(12);
+    else if (nch <= 16) SEL(16);
+    else if (nch <= 24) SEL(24);
+    else if (nch <= 32) SEL(32);
+    else if (nch <= 48) SEL(48);
+    else SEL(64);
+#undef SEL
 }
 
 template <int MAXC>
