@@ -36,6 +36,7 @@
 //                       block's stored scores and reads the block's V rows
 //                       (workgroups past the list exit at once), and
 //                       dec_combine_kernel merges those splits.
+// lambda = 0 drops nothing and runs the plain step.
 // Every sum has a fixed order, so results are bit-reproducible.
 #include "device_common.h"
 #include "stem_internal.h"
@@ -165,15 +166,20 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecArgs a) {
 }
 
 // Selection, one wave per (b, h): the keys of J = 64 c + lane in registers
-// (MAXC chunks), the want-th largest found by a bitwise search from the top,
-// equal keys to the smaller J; the kept list is written in ascending J.
+// (MAXC chunks; J outside [1, I-1] hold key 0), the threshold of the top-k by
+// topk_threshold (equal keys to the smaller J); the kept list is written in
+// ascending J.
 template <int MAXC>
 __global__ __launch_bounds__(64) void dec_select_kernel(DecArgs a) {
+    __shared__ uint32_t buf[64];
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const RowPlan rp = row_plan(a, b);
     const int I = rp.I, want = rp.want;
     int32_t *lrow = a.lists + ((size_t)b * a.hq + h) * a.nb;
-    if (lane == 0) a.counts[(size_t)b * a.hq + h] = rp.kk;
+    if (lane == 0) {
+        a.counts[(size_t)b * a.hq + h] = rp.kk;
+        if (a.skipped && !a.bmax) a.skipped[(size_t)b * a.hq + h] = 0;   // lambda = 0: nothing dropped
+    }
     if (want >= rp.ncand) {                         // every block up to I
         for (int j = lane; j <= I; j += kWave) lrow[j] = j;
         return;
@@ -185,41 +191,22 @@ __global__ __launch_bounds__(64) void dec_select_kernel(DecArgs a) {
         const int j = c * 64 + lane;
         key[c] = (j >= 1 && j < I) ? keys[j] : 0u;
     }
-    const int nch = (I + 63) >> 6;
-    uint32_t kmin = ~0u, kmax = 0u;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        const int j = c * 64 + lane;
-        if (c < nch && j >= 1 && j < I) {
-            kmin = min(kmin, key[c]);
-            kmax = max(kmax, key[c]);
-        }
-    }
-    int top;
-    uint32_t th = key_prefix(wave_min_u32(kmin), wave_max_u32(kmax), top);   // bits above top: common
-    for (int bit = top; bit >= 0; --bit) {
-        const uint32_t cand = th | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int c = 0; c < MAXC; ++c)
-            if (c < nch) cnt += __popcll(ballot64(key[c] >= cand));
-        if (cnt >= want) th = cand;
-    }
-    int gt = 0;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c)
-        if (c < nch) gt += __popcll(ballot64(key[c] > th));
-    const int need_eq = want - gt;
+    uint32_t th = 0u;
+    int need_eq = 0;
+    if (want > 0) topk_threshold<MAXC>(key, I, want, rp.ncand, buf, lane, th, need_eq);
     int run_eq = 0, run_keep = 0;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         if (c <= (I >> 6)) {                        // uniform; keeps the loop fully unrolled
             const int j = c * 64 + lane;
             const bool valid = j >= 1 && j < I;
-            const bool eq = valid && key[c] == th;
-            const uint64_t eqm = ballot64(eq);
-            bool keep = valid && (key[c] > th || (eq && run_eq + lanes_below(eqm) < need_eq));
-            run_eq += __popcll(eqm);
+            bool keep = false;
+            if (want > 0) {
+                const bool eq = valid && key[c] == th;
+                const uint64_t eqm = ballot64(eq);
+                keep = valid && (key[c] > th || (eq && run_eq + lanes_below(eqm) < need_eq));
+                run_eq += __popcll(eqm);
+            }
             keep = keep || j == 0 || j == I;
             const uint64_t km = ballot64(keep);
             if (keep) lrow[run_keep + lanes_below(km)] = j;
@@ -609,7 +596,10 @@ hipError_t launch_decode(const Shape &s, const void *q, const KvView &kv, const 
     a.k_scale = s.k_scale;
     a.v_scale = s.v_scale;
     a.tau = s.tau;
-    if (skip) {
+    // lambda = 0 drops nothing: the plain step, whose result it then is bit
+    // for bit (the selection reports zero dropped blocks)
+    const bool sk = skip != nullptr && skip->log2_lambda != -__builtin_huge_valf();
+    if (sk) {
         size_t obm, olv, onl, osc, tot2;
         decode_skip_layout(s, &obm, &olv, &onl, &osc, &tot2);
         a.bmax = reinterpret_cast<float *>(ws + obm);
@@ -618,8 +608,9 @@ hipError_t launch_decode(const Shape &s, const void *q, const KvView &kv, const 
         a.scores = reinterpret_cast<float *>(ws + osc);
         a.skipped = skip->skipped;
         a.skip_log2 = skip->log2_lambda;
+    } else if (skip) {
+        a.skipped = skip->skipped;
     }
-    const bool sk = skip != nullptr;
     if (s.d == 64) {
         switch (s.dtype) {
             case STEM_F32: return launch_blk<4, 64>(s, a, sk, st);

@@ -180,4 +180,84 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
+// Threshold of a top-k among keys held as key[c] for J = 64 c + lane (c < NCH),
+// the candidates being J in [1, I-1] (every other J holds key 0, which no
+// trial value counts): t is the want-th largest key, or a value with exactly
+// `want` keys at or above it; the kept set is every key > t plus the first
+// need_eq keys == t in J order.  Needs 0 < want < ncand = I - 1.
+// A bitwise search from the highest bit on which the candidates differ (the
+// bits above it are common to all of them, so to t as well).  While the
+// bucket of keys sharing t's decided bits holds more than 64 keys, each bit is
+// counted per lane on the VALU and summed across the wave once; then the
+// bucket is gathered into one key per lane through buf (64 u32 of LDS, this
+// wave's) and each further bit costs one ballot.
+template <int NCH>
+__device__ __forceinline__ void topk_threshold(const uint32_t (&key)[NCH], int I, int want, int ncand,
+                                               uint32_t *buf, int lane, uint32_t &t, int &need_eq) {
+    uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int j = c * 64 + lane;
+        kmin = min(kmin, (j >= 1 && j < I) ? key[c] : ~0u);
+        kmax = max(kmax, key[c]);              // invalid J: 0, and some J is valid here
+    }
+    int bit;
+    t = key_prefix(wave_min_u32(kmin), wave_max_u32(kmax), bit);
+    // The bucket: the keys whose bits above `bit` equal t's; `above` keys lie
+    // above it.  A trial value t | 2^bit is reached by the keys above the
+    // bucket and the bucket's keys with that bit set.
+    int above = 0, size = ncand;
+    for (; bit >= 0 && size > 64; --bit) {
+        const uint32_t cand = t | (1u << bit);
+        int cl = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) cl += key[c] >= cand ? 1 : 0;
+        const int cnt = __builtin_amdgcn_readfirstlane(wave_sum_i32(cl));
+        if (cnt >= want) {
+            t = cand;
+            size = cnt - above;
+        } else {
+            size -= cnt - above;
+            above = cnt;
+        }
+        // Exactly `want` keys are >= cand: they are the kept set whatever the
+        // lower bits hold, and the rule keeps every key > t and every key == t.
+        if (cnt == want) {
+            need_eq = want;                    // every key == t (there are want - #{> t} of them)
+            return;
+        }
+    }
+    if (bit >= 0) {
+        // gather the bucket (at most 64 keys) into one key per lane
+        const uint32_t hi = bit >= 31 ? 0u : ~0u << (bit + 1);
+        int run = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int j = c * 64 + lane;
+            const bool in = j >= 1 && j < I && ((key[c] ^ t) & hi) == 0u;
+            const uint64_t m = ballot64(in);
+            if (in) buf[run + lanes_below(m)] = key[c];
+            run += __popcll(m);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const uint32_t kb = lane < run ? buf[lane] : 0u;
+        for (; bit >= 0; --bit) {
+            const uint32_t cand = t | (1u << bit);
+            const int cnt = above + __popcll(ballot64(kb >= cand));
+            if (cnt >= want) t = cand;
+            if (cnt == want) {
+                need_eq = want;
+                return;
+            }
+        }
+        // t is the want-th largest key: the keys above it lie above the bucket or in it
+        need_eq = want - (above + __popcll(ballot64(kb > t)));
+        return;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) gt += __popcll(ballot64(key[c] > t));
+    need_eq = want - gt;
+}
+
 }  // namespace stem

@@ -46,74 +46,11 @@ __device__ __forceinline__ void select_row(const SelectArgs &a, long long row, i
         key[c] = (j >= 1 && j < I) ? order_key(x) : 0u;
     }
 
-    // Threshold key t: the want-th largest key, by a bitwise search from the
-    // highest bit on which the row's candidate keys differ (the bits above it
-    // are common to all of them, so to t as well).
+    // the threshold of the kept set (need_eq: keys equal to it still kept, smallest J first)
     uint32_t t = 0u;
-    int need_eq = 0;                           // keys == t still to keep, smallest J first
+    int need_eq = 0;
     const bool all = want >= ncand;
-    if (want > 0 && !all) {
-        uint32_t kmin = ~0u, kmax = 0u;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int j = c * 64 + lane;
-            kmin = min(kmin, (j >= 1 && j < I) ? key[c] : ~0u);
-            kmax = max(kmax, key[c]);          // invalid J: 0, and some J is valid here
-        }
-        int bit;
-        t = key_prefix(wave_min_u32(kmin), wave_max_u32(kmax), bit);
-        // The bucket: the keys whose bits above `bit` equal t's; `above` keys
-        // lie above it.  A trial value t | 2^bit is reached by the keys above
-        // the bucket and the bucket's keys with that bit set.
-        int above = 0, size = ncand;
-        bool found = false;
-        for (; bit >= 0 && size > 64; --bit) {
-            const uint32_t cand = t | (1u << bit);
-            int cl = 0;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) cl += key[c] >= cand ? 1 : 0;
-            const int cnt = __builtin_amdgcn_readfirstlane(wave_sum_i32(cl));
-            if (cnt >= want) {
-                t = cand;
-                size = cnt - above;
-            } else {
-                size -= cnt - above;
-                above = cnt;
-            }
-            // Exactly `want` keys are >= cand: they are the kept set whatever
-            // the lower bits hold, and with t = cand the rule below keeps
-            // every key > t and every key == t, i.e. exactly them.
-            if (cnt == want) {
-                found = true;
-                break;
-            }
-        }
-        if (!found && bit >= 0) {
-            // gather the bucket (at most 64 keys) into one key per lane, through LDS
-            const uint32_t hi = bit >= 31 ? 0u : ~0u << (bit + 1);
-            int run = 0;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int j = c * 64 + lane;
-                const bool in = j >= 1 && j < I && ((key[c] ^ t) & hi) == 0u;
-                const uint64_t m = ballot64(in);
-                if (in) buf[run + lanes_below(m)] = key[c];
-                run += __popcll(m);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            const uint32_t kb = lane < run ? buf[lane] : 0u;
-            for (; bit >= 0; --bit) {
-                const uint32_t cand = t | (1u << bit);
-                const int cnt = above + __popcll(ballot64(kb >= cand));
-                if (cnt >= want) t = cand;
-                if (cnt == want) break;
-            }
-        }
-        int gt = 0;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) gt += __popcll(ballot64(key[c] > t));
-        need_eq = want - gt;
-    }
+    if (want > 0 && !all) topk_threshold<NCH>(key, I, want, ncand, buf, lane, t, need_eq);
 
     // The kept set, chunk by chunk in J order; lane w collects mask words w,
     // w + 64, ... (two words per chunk).

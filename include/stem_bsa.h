@@ -241,7 +241,8 @@ int stem_decode_blasst_workspace_size(const stem_attn_desc *desc, size_t *bytes)
  * ln(1 / lambda) below the largest of the earlier kept blocks; the first kept
  * block never is.  O and LSE are those of the blocks not dropped.  The K rows
  * of every kept block are read; the V rows of a dropped block are not.
- *   lambda:  in [0, 1] (0 drops nothing); NaN or values outside are
+ *   lambda:  in [0, 1] (0 drops nothing: the step is stem_decode's, with
+ *            bit-identical O and LSE); NaN or values outside are
  *            STEM_EINVAL.
  *   skipped: optional int32 [batch, num_q_heads]: blocks each row dropped.
  *   workspace: at least stem_decode_blasst_workspace_size() bytes.
