@@ -1398,12 +1398,55 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     }
 
     // ---- merge the key halves, normalise, store -------------------------------
-    // The two waves of a query group each finalise two of the four d tiles
-    // (key half ks: tiles 2 ks, 2 ks + 1).  Each hands the other two tiles and
-    // its (M, l, lq) to its partner (wave ^ 4) through LDS.
+    // Sparse: the two waves of a query group each finalise two of the four d
+    // tiles (key half ks: tiles 2 ks, 2 ks + 1).  Each hands the other two tiles
+    // and its (M, l, lq) to its partner (wave ^ 4) through LDS.
     l = sum_xor32(l);                                      // exact sum of P: the LSE
     float lq = lacc[0];                                    // sum of the quantised P: O's denominator
     sync_vm<0, true>();                                    // every load into LDS is done: stages are free
+    if constexpr (!SPARSE) {
+    // Dense: the key-half-1 wave hands all four d tiles to its partner, which
+    // finalises them alone (measured faster for the dense kernel than the
+    // split below).
+    float *po = reinterpret_cast<float *>(smem) + wq * 64 * (D / 2);
+    if (ks == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) po[(dt * 16 + e) * 64 + lane] = o[dt][e];
+        part_ml[(3 * wq) * 64 + lane] = M;
+        part_ml[(3 * wq + 1) * 64 + lane] = l;
+        part_ml[(3 * wq + 2) * 64 + lane] = lq;
+    }
+    __syncthreads();
+    if (ks == 1) return;
+    const float M1 = part_ml[(3 * wq) * 64 + lane];
+    const float l1 = part_ml[(3 * wq + 1) * 64 + lane];
+    const float lq1 = part_ml[(3 * wq + 2) * 64 + lane];
+    const float mm = fmaxf(M, M1);
+    const float a0 = __builtin_amdgcn_exp2f(M - mm), a1 = __builtin_amdgcn_exp2f(M1 - mm);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] = fmaf(o[dt][e], a0, po[(dt * 16 + e) * 64 + lane] * a1);
+    l = fmaf(l, a0, l1 * a1);                            // key half 0 fused onto half 1: as the sparse merge
+    lq = fmaf(lq, a0, lq1 * a1);
+    const float inv = lq > 0.0f ? a.o_scale / lq : 0.0f;
+    const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * dt + 8 * i + 4 * g32;
+            u32x2 u;
+            u.x = f32_to_bf16_bits(o[dt][4 * i] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 1] * inv) << 16);
+            u.y = f32_to_bf16_bits(o[dt][4 * i + 2] * inv) | (f32_to_bf16_bits(o[dt][4 * i + 3] * inv) << 16);
+            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + obase + d0) = u;
+        }
+    if (a.lse && g32 == 0)
+        a.lse[((size_t)b * a.hq + h) * a.seq + token] = l > 0.0f ? fmaf(mm, 0.6931471805599453f, logf(l)) : ninf;
+    if (SKIP && a.skipped && g32 == 0) a.skipped[((size_t)b * a.hq + h) * a.seq + token] = nskip;
+    } else {
     auto hand_over = [&](auto KSC) {
         constexpr int K = decltype(KSC)::value;
         float *pout = reinterpret_cast<float *>(smem) + wave * (32 * 64);
@@ -1430,7 +1473,6 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         const float a0 = __builtin_amdgcn_exp2f(M0 - mm), a1 = __builtin_amdgcn_exp2f(M1 - mm);
         const float lt = fmaf(K ? lp : l, a0, (K ? l : lp) * a1);
         const float lqt = fmaf(K ? lqp : lq, a0, (K ? lq : lqp) * a1);
-        const float as = K ? a1 : a0, ap = K ? a0 : a1;   // own and partner's factor
         const float inv = lqt > 0.0f ? a.o_scale / lqt : 0.0f;
         const float *pin = reinterpret_cast<const float *>(smem) + pw * (32 * 64);
         const size_t obase = (((size_t)b * a.seq + token) * a.hq + h) * D;
@@ -1439,7 +1481,11 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             const int dt = 2 * K + u;
             f32x16 x;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) x[e] = fmaf(o[2 * K + u][e], as, pin[(u * 16 + e) * 64 + lane] * ap) * inv;
+            for (int e = 0; e < 16; ++e) {
+                // key half 0's value fused onto half 1's product, on either wave
+                const float own = o[2 * K + u][e], other = pin[(u * 16 + e) * 64 + lane];
+                x[e] = fmaf(K ? other : own, a0, (K ? own : other) * a1) * inv;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d0 = 32 * dt + 8 * i + 4 * g32;
@@ -1455,6 +1501,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
     };
     if (ks == 0) finish(integral_constant<int, 0>{});
     else finish(integral_constant<int, 1>{});
+    }
     };
     const int rows = a.batch * a.hq * a.nb;
     if (SPARSE && (int)blockIdx.x < rows) wcur = mask_word(a, persistent_row(a, blockIdx.x, 0), threadIdx.x);
