@@ -94,6 +94,7 @@ int check_kv(const stem_kv_desc *kv, const Shape &s, KvView *out) {
     out->table = kv->block_table;
     out->page_log2 = 0;
     out->pages_per_seq = 0;
+    out->rows = (size_t)s.batch * s.seq;
     if (kv->block_table) {
         const int p = kv->page_size;
         if (p < 1 || (p & (p - 1))) return fail(STEM_EINVAL, "page_size %d is not a power of two", p);
@@ -104,6 +105,7 @@ int check_kv(const stem_kv_desc *kv, const Shape &s, KvView *out) {
         while ((1 << lg) < p) ++lg;
         out->page_log2 = lg;
         out->pages_per_seq = kv->pages_per_seq;
+        out->rows = (size_t)kv->num_pages * p;
     }
     return STEM_OK;
 }

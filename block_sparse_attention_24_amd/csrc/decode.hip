@@ -76,6 +76,7 @@ struct DecArgs {
     int32_t *skipped;                 // [b, hq] dropped entries, or null
     float skip_log2;                  // log2(lambda)
     int hq, hkv, d, blk, nb, seq, nsplit;
+    int off32;                        // K/V byte offsets fit in 32 bits
     float q_scale, k_scale, v_scale, tau;
 };
 
@@ -218,8 +219,9 @@ __global__ __launch_bounds__(64) void dec_select_kernel(DecArgs a) {
 // ---------------------------------------------------------------------------
 // Split-K attention over the kept blocks
 // ---------------------------------------------------------------------------
-template <int ES, int D, int BLK, int MODE>
-__global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
+// fp8 with 32-bit offsets fits in 96 registers: five workgroups per CU
+template <int ES, int D, int BLK, int MODE, typename OFF>
+__global__ __launch_bounds__(256, (ES == 1 && sizeof(OFF) == 4) ? 5 : 1) void dec_attn_kernel(DecArgs a) {
     constexpr int CPR = D * ES / 16;                // 16-byte chunks per K/V row
     constexpr int RPP = kWave / CPR;                // rows per pass
     constexpr int EPC = 16 / ES;                    // elements per chunk
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
         // byte offset of each pass's row (rows past nkeys read row nkeys-1, then
         // masked).  Paged: the block's page entries (at most BLK/16) are read
         // once, one per lane, and handed to the rows by lane shuffles.
-        size_t roff[NP];
+        OFF roff[NP];                                   // 32-bit when the K/V tensors are below 4 GiB
         if (a.table) {
             const int lg = a.page_log2;
             const int pg0 = tok0 >> lg;
@@ -288,13 +290,13 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
             for (int p = 0; p < NP; ++p) {
                 const int tok = tok0 + min(p * RPP + r, nkeys - 1);
                 const int page = __shfl(pg_lane, (tok >> lg) - pg0);
-                roff[p] = (((size_t)page << lg) + (tok & ((1 << lg) - 1))) * row_bytes + col;
+                roff[p] = (OFF)((((size_t)page << lg) + (tok & ((1 << lg) - 1))) * row_bytes + col);
             }
         } else {
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 const int tok = tok0 + min(p * RPP + r, nkeys - 1);
-                roff[p] = ((size_t)b * a.seq + tok) * row_bytes + col;
+                roff[p] = (OFF)(((size_t)b * a.seq + tok) * row_bytes + col);
             }
         }
         if constexpr (MODE == kPV) {
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecArgs a) {
         auto src_of = [&](int i) { return MODE == kPV ? a.v : (i < NP ? a.k : a.v); };
         uint4 ring[DIST];
         auto issue = [&](int i) {
-            ring[i % DIST] = *reinterpret_cast<const uint4 *>(src_of(i) + roff[i % NP]);
+            ring[i % DIST] = *reinterpret_cast<const uint4 *>(src_of(i) + (size_t)roff[i % NP]);
         };
 #pragma unroll
         for (int i = 0; i < DIST; ++i) issue(i);
@@ -521,11 +523,14 @@ hipError_t launch_all(const Shape &s, DecArgs &a, bool skip, hipStream_t st) {
     else hipLaunchKernelGGL((dec_select_kernel<64>), heads, dim3(64), 0, st, a);
     const dim3 splits(a.nsplit, s.hq, s.batch);
     if (skip) {
-        hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kQK>), splits, dim3(256), 0, st, a);
+        if (a.off32) hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kQK, uint32_t>), splits, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kQK, size_t>), splits, dim3(256), 0, st, a);
         hipLaunchKernelGGL(dec_prefix_kernel, heads, dim3(64), 0, st, a);
-        hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kPV>), splits, dim3(256), 0, st, a);
+        if (a.off32) hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kPV, uint32_t>), splits, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kPV, size_t>), splits, dim3(256), 0, st, a);
     } else {
-        hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kFull>), splits, dim3(256), 0, st, a);
+        if (a.off32) hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kFull, uint32_t>), splits, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((dec_attn_kernel<ES, D, BLK, kFull, size_t>), splits, dim3(256), 0, st, a);
     }
     hipLaunchKernelGGL((dec_combine_kernel<D>), heads, dim3(256), 0, st, a, ES == 4 ? 1 : 0);
     return hipGetLastError();
@@ -592,6 +597,8 @@ hipError_t launch_decode(const Shape &s, const void *q, const KvView &kv, const 
     a.nb = s.nb;
     a.seq = s.seq;
     a.nsplit = (s.nb + kSplit - 1) / kSplit;
+    const size_t es = s.dtype == STEM_F32 ? 4 : s.dtype == STEM_BF16 ? 2 : 1;
+    a.off32 = kv.rows * s.hkv * s.d * es < (size_t(1) << 32) ? 1 : 0;
     a.q_scale = s.q_scale;
     a.k_scale = s.k_scale;
     a.v_scale = s.v_scale;

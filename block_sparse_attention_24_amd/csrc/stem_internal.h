@@ -24,6 +24,7 @@ struct KvView {
     const int32_t *table;
     int page_log2;
     int pages_per_seq;
+    size_t rows;                      // token rows of each of K and V (pages x page_size when paged)
 };
 
 // The TPD budget in closed form: every row's budget follows from the single

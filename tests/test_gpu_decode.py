@@ -251,3 +251,46 @@ def test_decode_full_128k_sampled_heads():
         r = dict(q=qd[:, hs], k=kd, v=vd, keep=[budget[nb - 1]], o=o[:, hs], lse=lse[:, hs],
                  lists=lists[hs][None], counts=np.full((1, group), budget[nb - 1]))
         _check(sub, r)
+
+
+def test_decode_cache_beyond_4gib():
+    """A paged FP8 cache of more than 4 GiB per tensor, with the sequence's pages
+    placed past the 4 GiB mark: the decode step takes its 64-bit-offset kernels
+    (below 4 GiB it uses 32-bit offsets) and returns, bit for bit, what the same
+    pages give in a small cache."""
+    case = Case(wl.Workload("dec-fp8-paged64-beyond4g", 1, 128 * 12, 4, 1, 128, 128, "fp8", paged=True,
+                            page_size=64), [128 * 12 - 3])
+    w = case.w
+    _announce(f"decode {w.name}")
+    src = wl.make_cache_inputs(w, device="cpu")
+    p = sb.Problem(w.batch, w.seq, w.hq, w.hkv, w.head_dim, w.block, w.dtype, 1.0,
+                   float(src["k_scale"]), float(src["v_scale"]))
+    table = src["block_table"].to(DEV)
+    small = (src["num_pages"], w.page_size, w.hkv, w.head_dim)
+    kc = torch.empty(small, dtype=torch.float8_e4m3fn, device=DEV)
+    vc = torch.empty_like(kc)
+    kbar, lvn = sb.cache_write(p, src["k"].to(DEV), src["v"].to(DEV), kc, vc, table, w.page_size)
+    page_bytes = w.page_size * w.hkv * w.head_dim                 # one byte per element
+    shift = (1 << 32) // page_bytes                                # pages below the 4 GiB mark
+    big = (shift + src["num_pages"], w.page_size, w.hkv, w.head_dim)
+    kb = torch.empty(big, dtype=torch.float8_e4m3fn, device=DEV)   # 4 GiB and more, left unwritten below
+    vb = torch.empty_like(kb)
+    kb[shift:] = kc
+    vb[shift:] = vc
+    table_big = (table + shift).contiguous()
+    q, q_scale = _query(w, 11)
+    p.q_scale = q_scale
+    q = q.to(DEV)
+    lens = torch.tensor(case.lens, dtype=torch.int32, device=DEV)
+    keep = torch.tensor(_keep_values(case, case.lens), dtype=torch.int32, device=DEV)
+    outs = []
+    for k_, v_, t_ in ((kc, vc, table), (kb, vb, table_big)):
+        o = torch.empty((w.batch, w.hq, w.head_dim), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device=DEV)
+        ws = torch.empty(sb.stem_decode_workspace_size(p), dtype=torch.uint8, device=DEV)
+        sb.stem_decode(p, q, k_, v_, lens, keep, kbar, lvn, o, lse, ws, t_, w.page_size)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    del kb, vb
+    torch.cuda.empty_cache()
