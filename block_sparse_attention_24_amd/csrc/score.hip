@@ -290,16 +290,21 @@ hipError_t pool_all(const Shape &s, const void *q, const KvView *kv, float *qbar
 }
 
 // ---------------------------------------------------------------------------
-// Score GEMM on the matrix cores (v_mfma_f32_32x32x2f32, fp32 in and out).  A
-// workgroup owns a 128 x 128 tile of (I, J) on or below the diagonal, each of
-// its four waves a 64 x 64 quarter held as 2 x 2 MFMA tiles; a quarter wholly
-// above the diagonal returns at once, and elements with J > I are not stored.  Per chunk of 8 dimensions a lane loads
-// four consecutive floats of one qbar row and of one kbar row straight from
-// global memory (lanes 0-31 dimensions d0..d0+3, lanes 32-63 d0+4..d0+7), so
-// MFMA step c of the chunk pairs dimension d0+c with d0+4+c.  The order of
-// the sum is fixed, so the scores are bit-reproducible.  Workgroups are
-// renumbered so that each XCD (workgroup id mod 8) takes a contiguous eighth
-// of the heads and reads their representations into its own L2.
+// Score GEMM on the matrix cores, bf16 MFMA (v_mfma_f32_32x32x16_bf16) on a
+// two-term split of each fp32 operand: x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi), and q.k summed as hi.hi + hi.lo + lo.hi in fp32.  The
+// dropped lo.lo term and the rounding of lo leave each product within about
+// 3 * 2^-18 of |q_i k_i|, a 16-bit-significand product at a tenth of the
+// fp32 MFMA time.  A workgroup owns a 128 x 128 tile of (I, J) on or below
+// the diagonal, each of its four waves a 64 x 64 quarter held as 2 x 2 MFMA
+// tiles; a quarter wholly above the diagonal returns at once, and elements
+// with J > I are not stored.  Per chunk of 16 dimensions a lane loads eight
+// consecutive floats of one qbar row and of one kbar row straight from global
+// memory (lanes 0-31 dimensions d0..d0+7, lanes 32-63 d0+8..d0+15), the
+// operand layout of the 32x32x16 MFMA.  The order of the sum is fixed, so
+// the scores are bit-reproducible.  Workgroups are renumbered so that each
+// XCD (workgroup id mod 8) takes a contiguous eighth of the heads and reads
+// their representations into its own L2.
 // ---------------------------------------------------------------------------
 constexpr int kTile = 128;
 
@@ -335,8 +340,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     if (I0 >= a.nb || J0 >= a.nb) return;      // nothing of this quarter is stored
     if (J0 > I0 + 63) return;                   // wholly above the diagonal: not written
 
-    const float *qb = a.qbar + ((size_t)b * a.hq + h) * a.nb * D + 4 * kh;
-    const float *kb = a.kbar + ((size_t)b * a.hkv + g) * a.nb * D + 4 * kh;
+    const float *qb = a.qbar + ((size_t)b * a.hq + h) * a.nb * D + 8 * kh;
+    const float *kb = a.kbar + ((size_t)b * a.hkv + g) * a.nb * D + 8 * kh;
     const float *qr[2], *kr[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {     // rows past the end read the last row; never stored
@@ -344,54 +349,85 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         kr[i] = kb + (size_t)min(J0 + 32 * i + r, a.nb - 1) * D;
     }
 
+    // value term of this lane's two columns, loaded ahead of the operands so
+    // that the waits of the loop cover it: read between the conditional
+    // stores below, it would make every store wait for the one before
+    const float *lv = a.lvn ? a.lvn + ((size_t)b * a.hkv + g) * a.nb : nullptr;
+    float lj[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lj[j] = lv ? lv[min(J0 + 32 * j + r, a.nb - 1)] : 0.0f;
+
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // three-deep ring: chunk n + 2 is requested before chunk n is multiplied
-    constexpr int NC = D / 8;
-    f32x4 A[3][2], B[3][2];
+    // four-deep ring: chunk n + 3 is requested before chunk n is multiplied
+    // (a load from L2 takes about a thousand cycles; a chunk's twelve MFMAs
+    // take a few hundred)
+    constexpr int NC = D / 16, RING = 4;
+    f32x4 A[RING][2][2], B[RING][2][2];                // [ring][tile][half of the 8 floats]
     auto load = [&](int n) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            A[n % 3][i] = *reinterpret_cast<const f32x4 *>(qr[i] + 8 * n);
-            B[n % 3][i] = *reinterpret_cast<const f32x4 *>(kr[i] + 8 * n);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                A[n % RING][i][u] = *reinterpret_cast<const f32x4 *>(qr[i] + 16 * n + 4 * u);
+                B[n % RING][i][u] = *reinterpret_cast<const f32x4 *>(kr[i] + 16 * n + 4 * u);
+            }
+    };
+    auto split = [](const f32x4 (&x)[2], bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = x[e >> 2][e & 3];
+            const __bf16 t = (__bf16)v;
+            hi[e] = t;
+            lo[e] = (__bf16)(v - (float)t);
         }
     };
-    load(0);
-    __builtin_amdgcn_sched_barrier(0);
-    load(1);
-    __builtin_amdgcn_sched_barrier(0);
+    auto mfma = [](const bf16x8 &x, const bf16x8 &y, const f32x16 &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+    };
+#pragma unroll
+    for (int n = 0; n < RING - 1 && n < NC; ++n) load(n);
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        if (n + 2 < NC) load(n + 2);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[n % 3][i][c], B[n % 3][j][c],
-                                                                     acc[i][j], 0, 0, 0);
+        if (n + RING - 1 < NC) load(n + RING - 1);
         __builtin_amdgcn_sched_barrier(0);
+        bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            split(A[n % RING][i], ah[i], al[i]);
+            split(B[n % RING][i], bh[i], bl[i]);
+        }
+        // small terms first, then hi.hi; four independent accumulators apart
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma(al[i], bh[j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma(ah[i], bl[j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma(ah[i], bh[j], acc[i][j]);
     }
 
     // lane holds column J0 + 32 j + r and rows I0 + 32 i + 8 (v / 4) + 4 kh + v % 4
-    const float *lv = a.lvn ? a.lvn + ((size_t)b * a.hkv + g) * a.nb : nullptr;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int J = J0 + 32 * j + r;
         if (J >= a.nb) continue;
-        const float lj = lv ? lv[J] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int I = I0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
-                if (I < a.nb && J <= I) out[(size_t)I * a.nb + J] = fmaf(acc[i][j][v], a.tau, lj);
+                if (I < a.nb && J <= I) out[(size_t)I * a.nb + J] = fmaf(acc[i][j][v], a.tau, lj[j]);
             }
     }
 }
