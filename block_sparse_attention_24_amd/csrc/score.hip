@@ -297,14 +297,13 @@ hipError_t pool_all(const Shape &s, const void *q, const KvView *kv, float *qbar
 // 3 * 2^-18 of |q_i k_i|, a 16-bit-significand product at a tenth of the
 // fp32 MFMA time.  A workgroup owns a 128 x 128 tile of (I, J) on or below
 // the diagonal, each of its four waves a 64 x 64 quarter held as 2 x 2 MFMA
-// tiles; a quarter wholly above the diagonal returns at once, and elements
-// with J > I are not stored.  Per chunk of 16 dimensions a lane loads eight
-// consecutive floats of one qbar row and of one kbar row straight from global
-// memory (lanes 0-31 dimensions d0..d0+7, lanes 32-63 d0+8..d0+15), the
-// operand layout of the 32x32x16 MFMA.  The order of the sum is fixed, so
-// the scores are bit-reproducible.  Workgroups are renumbered so that each
-// XCD (workgroup id mod 8) takes a contiguous eighth of the heads and reads
-// their representations into its own L2.
+// tiles; a quarter wholly above the diagonal is not computed, and elements
+// with J > I are not stored.  The tile's qbar and kbar rows pass through LDS
+// in chunks of 32 dimensions, split once as they are written (two stages:
+// the next chunk is written while this one is multiplied).  The order of the
+// sum is fixed, so the scores are bit-reproducible.  Workgroups are
+// renumbered so that each XCD (workgroup id mod 8) takes a contiguous eighth
+// of the heads and reads their representations into its own L2.
 // ---------------------------------------------------------------------------
 constexpr int kTile = 128;
 
@@ -335,19 +334,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 
     const int w = tid >> 6, lane = tid & 63;
     const int r = lane & 31, kh = lane >> 5;
-    const int I0 = ti * kTile + (w >> 1) * 64;
-    const int J0 = tj * kTile + (w & 1) * 64;
-    if (I0 >= a.nb || J0 >= a.nb) return;      // nothing of this quarter is stored
-    if (J0 > I0 + 63) return;                   // wholly above the diagonal: not written
-
-    const float *qb = a.qbar + ((size_t)b * a.hq + h) * a.nb * D + 8 * kh;
-    const float *kb = a.kbar + ((size_t)b * a.hkv + g) * a.nb * D + 8 * kh;
-    const float *qr[2], *kr[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {     // rows past the end read the last row; never stored
-        qr[i] = qb + (size_t)min(I0 + 32 * i + r, a.nb - 1) * D;
-        kr[i] = kb + (size_t)min(J0 + 32 * i + r, a.nb - 1) * D;
-    }
+    const int TI = ti * kTile, TJ = tj * kTile;         // the workgroup's tile
+    if (TI >= a.nb || TJ >= a.nb) return;               // (whole workgroup: uniform)
+    const int I0 = TI + (w >> 1) * 64;
+    const int J0 = TJ + (w & 1) * 64;
+    // a quarter wholly above the diagonal, or past the end, is not computed;
+    // its wave still stages operands for the others
+    const bool live = I0 < a.nb && J0 < a.nb && J0 <= I0 + 63;
 
     // value term of this lane's two columns, loaded ahead of the operands so
     // that the waits of the loop cover it: read between the conditional
@@ -357,65 +350,108 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) lj[j] = lv ? lv[min(J0 + 32 * j + r, a.nb - 1)] : 0.0f;
 
+    // Staging: per chunk of 32 dimensions the workgroup loads the tile's 128
+    // qbar rows and 128 kbar rows (rows past the end read the last row; their
+    // results are never stored), splits each float once into bf16 hi and lo
+    // and writes the four planes [Q hi, Q lo, K hi, K lo] of 128 rows x 64
+    // bytes into one of two LDS stages.  Thread t moves 4-dim groups
+    // t + 256 u (u = 0..3) of each operand: row (t + 256 u) / 8, group t % 8.
+    // The 16-byte chunk c of row x sits at position c ^ ((x >> 2) & 3), so
+    // the MFMA reads (16 rows, one chunk each) fall in distinct banks.
+    constexpr int CH = 32, NC = D / CH, PLANE = 128 * CH * 2, STAGE = 4 * PLANE;
+    __shared__ __attribute__((aligned(16))) char st[2 * STAGE];
+    const float *qsrc[4], *ksrc[4];
+    int woff[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int x = (tid + 256 * u) >> 3, c4 = tid & 7;
+        qsrc[u] = a.qbar + (((size_t)b * a.hq + h) * a.nb + min(TI + x, a.nb - 1)) * D + 4 * c4;
+        ksrc[u] = a.kbar + (((size_t)b * a.hkv + g) * a.nb + min(TJ + x, a.nb - 1)) * D + 4 * c4;
+        woff[u] = x * 64 + (((c4 >> 1) ^ ((x >> 2) & 3)) << 4) + 8 * (c4 & 1);
+    }
+    f32x4 gq[4], gk[4];
+    auto fetch = [&](int c) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            gq[u] = *reinterpret_cast<const f32x4 *>(qsrc[u] + CH * c);
+            gk[u] = *reinterpret_cast<const f32x4 *>(ksrc[u] + CH * c);
+        }
+    };
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    auto put = [&](int stage) {
+        char *base = st + stage * STAGE;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int op = 0; op < 2; ++op) {
+                const f32x4 &x = op ? gk[u] : gq[u];
+                bf16x4 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const __bf16 t = (__bf16)x[e];
+                    hi[e] = t;
+                    lo[e] = (__bf16)(x[e] - (float)t);
+                }
+                *reinterpret_cast<bf16x4 *>(base + (2 * op) * PLANE + woff[u]) = hi;
+                *reinterpret_cast<bf16x4 *>(base + (2 * op + 1) * PLANE + woff[u]) = lo;
+            }
+    };
+    // MFMA operand of k step s (16 dimensions) for tile rows x0 + r: this
+    // lane's 8 dimensions 16 s + 8 kh, chunk 2 s + kh of the row
+    auto opnd = [&](int stage, int plane, int x0, int s) {
+        const int x = x0 + r;
+        return *reinterpret_cast<const bf16x8 *>(st + stage * STAGE + plane * PLANE + x * 64 +
+                                                 (((2 * s + kh) ^ ((x >> 2) & 3)) << 4));
+    };
+    auto mfma = [](const bf16x8 &x, const bf16x8 &y, const f32x16 &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+    };
+
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // four-deep ring: chunk n + 3 is requested before chunk n is multiplied
-    // (a load from L2 takes about a thousand cycles; a chunk's twelve MFMAs
-    // take a few hundred)
-    constexpr int NC = D / 16, RING = 4;
-    f32x4 A[RING][2][2], B[RING][2][2];                // [ring][tile][half of the 8 floats]
-    auto load = [&](int n) {
+    const int xi = (w >> 1) * 64, xj = (w & 1) * 64;   // the quarter's rows within the tile
+    fetch(0);
+    put(0);
+    if (NC > 1) fetch(1);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+    for (int c = 0; c < NC; ++c) {
+        __syncthreads();                                // stage c & 1 written; the other one free
+        if (c + 1 < NC) {
+            put((c + 1) & 1);
+            if (c + 2 < NC) fetch(c + 2);
+        }
+        if (live) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                A[n % RING][i][u] = *reinterpret_cast<const f32x4 *>(qr[i] + 16 * n + 4 * u);
-                B[n % RING][i][u] = *reinterpret_cast<const f32x4 *>(kr[i] + 16 * n + 4 * u);
+            for (int s = 0; s < CH / 16; ++s) {
+                bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    ah[i] = opnd(c & 1, 0, xi + 32 * i, s);
+                    al[i] = opnd(c & 1, 1, xi + 32 * i, s);
+                    bh[i] = opnd(c & 1, 2, xj + 32 * i, s);
+                    bl[i] = opnd(c & 1, 3, xj + 32 * i, s);
+                }
+                // small terms first, then hi.hi; four independent accumulators apart
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma(al[i], bh[j], acc[i][j]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma(ah[i], bl[j], acc[i][j]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma(ah[i], bh[j], acc[i][j]);
             }
-    };
-    auto split = [](const f32x4 (&x)[2], bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float v = x[e >> 2][e & 3];
-            const __bf16 t = (__bf16)v;
-            hi[e] = t;
-            lo[e] = (__bf16)(v - (float)t);
         }
-    };
-    auto mfma = [](const bf16x8 &x, const bf16x8 &y, const f32x16 &c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
-    };
-#pragma unroll
-    for (int n = 0; n < RING - 1 && n < NC; ++n) load(n);
-#pragma unroll
-    for (int n = 0; n < NC; ++n) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (n + RING - 1 < NC) load(n + RING - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 ah[2], al[2], bh[2], bl[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            split(A[n % RING][i], ah[i], al[i]);
-            split(B[n % RING][i], bh[i], bl[i]);
-        }
-        // small terms first, then hi.hi; four independent accumulators apart
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma(al[i], bh[j], acc[i][j]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma(ah[i], bl[j], acc[i][j]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma(ah[i], bh[j], acc[i][j]);
     }
+    if (!live) return;
 
     // lane holds column J0 + 32 j + r and rows I0 + 32 i + 8 (v / 4) + 4 kh + v % 4
 #pragma unroll
