@@ -1206,9 +1206,11 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         i32x8 va = PH == 1 ? i32x8{} : vop(VRD, 0);
         i32x8 plo = {};                                    // PH == 1: residual of P(0)
         // the decision, after the first operand reads so that their latency and
-        // the other half's maximum overlap; soft: some row of the wave keeps
-        // block j (always, without the skip); the softmax slices are branched
-        // over, wave-uniformly, when none does
+        // the other half's maximum overlap.  A row that drops block j runs its
+        // softmax like the others with an exp2 offset of +inf: its P are 0 and
+        // its M, l and O stay as they are.  (Branching the softmax over when
+        // the whole wave drops the block costs registers and spills in every
+        // block, for a saving only in the rare blocks all 32 rows drop.)
         bool skip = false;
         if constexpr (SKIP) {
             const float xb = fmaxf(hmine, hother) * c;     // block j's max for this row, log2 units
@@ -1216,7 +1218,6 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             pmax = fmaxf(pmax, xb);
             nskip += skip ? 1 : 0;
         }
-        const bool soft = SKIP ? !__all(skip) : true;
         // row max: a tree of three-input maxima (v_max3), 16 for the 32 scores
         auto max3 = [](float x, float y, float z) { return fmaxf(x, fmaxf(y, z)); };
         auto tile_max = [&](const f32x16 &x, float &u, float &v) {
@@ -1231,7 +1232,7 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         dma_k(integral_constant<int, 0>{});
         ka = kop(KRD, 0, 1);
         float ce = 0.0f, mc = 0.0f;
-        if (soft) {
+        {
             float mx;                                      // this half's max of block j (raw)
             if constexpr (SKIP) {
                 mx = hmine;
@@ -1283,11 +1284,8 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
             for (int e = 4 * (q & 3); e < 4 * (q & 3) + 4; ++e) ls[e & 3] = q == 0 ? sc[0][e] : ls[e & 3] + sc[q >> 2][e];
             packq(q);
         };
-        // one softmax slice per MFMA slot, skipped as a whole (one wave-uniform
-        // branch) when no row of the wave keeps block j
-        auto slice = [&](auto f) {
-            if (soft) f();
-        };
+        // one softmax slice per MFMA slot
+        auto slice = [&](auto f) { f(); };
         slice([&] { fq(0); });
         SB();
         sn[1] = mfma8(kb, qop(0), f32x16{}, 127);
@@ -1338,14 +1336,10 @@ __global__ __launch_bounds__(512, 1) void bsa_fp8_kernel(BsaArgs a) {
         if constexpr (PH != 1) lacc = mfma8(ones, pv_in, lacc, psc_in);
         SB();
         slice([&] { aq(6); aq(7); });
-        if (soft) {
+        {
             const int ice = (int)ce;
             l = fmaf(l, alpha, ldexpf((ls[0] + ls[1]) + (ls[2] + ls[3]), ice - 8));
             psc_out = 119 + ice;
-        } else {
-            pv_out = i32x8{};                              // P(j) = 0: PV(j) adds nothing
-            psc_out = 127;
-            alpha = 1.0f;                                  // M, l unchanged
         }
         SB();
         if constexpr (PH == 1) {
