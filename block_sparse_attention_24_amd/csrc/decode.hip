@@ -194,7 +194,8 @@ __global__ __launch_bounds__(64) void dec_select_kernel(DecArgs a) {
     }
     uint32_t th = 0u;
     int need_eq = 0;
-    if (want > 0) topk_threshold<MAXC>(key, I, want, rp.ncand, buf, lane, th, need_eq);
+    bool all_eq = true;
+    if (want > 0) topk_threshold<MAXC>(key, I, want, rp.ncand, buf, lane, th, need_eq, all_eq);
     int run_eq = 0, run_keep = 0;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {

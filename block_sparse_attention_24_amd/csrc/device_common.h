@@ -190,10 +190,13 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // bucket of keys sharing t's decided bits holds more than 64 keys, each bit is
 // counted per lane on the VALU and summed across the wave once; then the
 // bucket is gathered into one key per lane through buf (64 u32 of LDS, this
-// wave's) and each further bit costs one ballot.
+// wave's) and each further bit costs one ballot.  all_eq: every key == t is
+// kept (need_eq covers them all), so the kept set is simply the keys >= t.
 template <int NCH>
 __device__ __forceinline__ void topk_threshold(const uint32_t (&key)[NCH], int I, int want, int ncand,
-                                               uint32_t *buf, int lane, uint32_t &t, int &need_eq) {
+                                               uint32_t *buf, int lane, uint32_t &t, int &need_eq,
+                                               bool &all_eq) {
+    all_eq = true;
     uint32_t kmin = ~0u, kmax = 0u;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -250,14 +253,17 @@ __device__ __forceinline__ void topk_threshold(const uint32_t (&key)[NCH], int I
                 return;
             }
         }
-        // t is the want-th largest key: the keys above it lie above the bucket or in it
+        // t is the want-th largest key: the keys above it lie above the bucket
+        // or in it, and the keys equal to it all lie in it
         need_eq = want - (above + __popcll(ballot64(kb > t)));
+        all_eq = need_eq >= __popcll(ballot64(kb == t));
         return;
     }
     int gt = 0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) gt += __popcll(ballot64(key[c] > t));
     need_eq = want - gt;
+    all_eq = need_eq >= size;                      // every bit decided: the bucket is the keys == t
 }
 
 }  // namespace stem

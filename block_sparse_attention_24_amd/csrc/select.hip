@@ -7,7 +7,9 @@
 // sink J=0 and the diagonal J=I are kept; the best k_I - |{0,I}| candidates
 // J in [1, I-1] are found by a bitwise search for the k-th largest
 // order-preserving 32-bit key (scores held in registers), then ties at the
-// threshold go to the smallest J by a prefix count over the lanes in J order.
+// threshold go to the smallest J by a prefix count over the lanes in J order
+// (when every key equal to the threshold is kept, which is the usual case,
+// the kept candidates are simply the keys at or above it).
 // The search counts on the VALU (per-lane counts, one wave sum per bit) while
 // the bucket of keys that share the threshold's decided bits holds more than
 // 64 keys; then that bucket is gathered into one key per lane and each
@@ -49,8 +51,12 @@ __device__ __forceinline__ void select_row(const SelectArgs &a, long long row, i
     // the threshold of the kept set (need_eq: keys equal to it still kept, smallest J first)
     uint32_t t = 0u;
     int need_eq = 0;
+    bool all_eq = false;
     const bool all = want >= ncand;
-    if (want > 0 && !all) topk_threshold<NCH>(key, I, want, ncand, buf, lane, t, need_eq);
+    if (want > 0 && !all) topk_threshold<NCH>(key, I, want, ncand, buf, lane, t, need_eq, all_eq);
+    // no tie to break at the threshold: the kept candidates are the keys >= t
+    // (invalid J hold key 0, below any t > 0)
+    const bool simple = want > 0 && !all && all_eq && t > 0u;
 
     // The kept set, chunk by chunk in J order; lane w collects mask words w,
     // w + 64, ... (two words per chunk).
@@ -59,20 +65,9 @@ __device__ __forceinline__ void select_row(const SelectArgs &a, long long row, i
     uint32_t mword[MW];
 #pragma unroll
     for (int q = 0; q < MW; ++q) mword[q] = 0u;
-    int run_eq = 0, run_keep = 0;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    int run_keep = 0;
+    auto emit = [&](int c, bool keep) {         // chunk c's kept J: its two mask words and list entries
         const int j = c * 64 + lane;
-        const bool valid = j >= 1 && j < I;
-        bool keep = false;
-        if (all) {                              // uniform branches: ballots stay wave-wide
-            keep = valid && want > 0;
-        } else if (want > 0) {
-            const bool eq = valid && key[c] == t;
-            const uint64_t eqm = ballot64(eq);
-            keep = valid && (key[c] > t || (eq && run_eq + lanes_below(eqm) < need_eq));
-            run_eq += __popcll(eqm);
-        }
         keep = keep || j == 0 || j == I;
         const uint64_t km = ballot64(keep);
         if ((lane >> 1) == (c & 31)) mword[c >> 5] = (lane & 1) ? (uint32_t)(km >> 32) : (uint32_t)km;
@@ -80,6 +75,27 @@ __device__ __forceinline__ void select_row(const SelectArgs &a, long long row, i
             const int pos = run_keep + lanes_below(km);
             if (keep && pos < a.list_stride) lrow[pos] = j;
             run_keep += __popcll(km);
+        }
+    };
+    if (simple) {                               // uniform branches: ballots stay wave-wide
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) emit(c, key[c] >= t);
+    } else {
+        int run_eq = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int j = c * 64 + lane;
+            const bool valid = j >= 1 && j < I;
+            bool keep = false;
+            if (all) {
+                keep = valid && want > 0;
+            } else if (want > 0) {
+                const bool eq = valid && key[c] == t;
+                const uint64_t eqm = ballot64(eq);
+                keep = valid && (key[c] > t || (eq && run_eq + lanes_below(eqm) < need_eq));
+                run_eq += __popcll(eqm);
+            }
+            emit(c, keep);
         }
     }
     uint32_t *mrow = a.mask + row * a.words;
