@@ -220,15 +220,18 @@ __global__ __launch_bounds__(64) void dec_select_kernel(DecArgs a) {
 // ---------------------------------------------------------------------------
 // Split-K attention over the kept blocks
 // ---------------------------------------------------------------------------
-// fp8 with 32-bit offsets fits in 96 registers: five workgroups per CU
+// fp8 with 32-bit offsets fits in 80 registers: six workgroups per CU (more
+// workgroups in flight beat a deeper ring of loads per lane: 8 in flight at
+// five per CU and 16 at four were slower)
 template <int ES, int D, int BLK, int MODE, typename OFF>
-__global__ __launch_bounds__(256, (ES == 1 && sizeof(OFF) == 4) ? 5 : 1) void dec_attn_kernel(DecArgs a) {
+__global__ __launch_bounds__(256, (ES == 1 && sizeof(OFF) == 4) ? 6 : 1) void dec_attn_kernel(DecArgs a) {
     constexpr int CPR = D * ES / 16;                // 16-byte chunks per K/V row
     constexpr int RPP = kWave / CPR;                // rows per pass
     constexpr int EPC = 16 / ES;                    // elements per chunk
     constexpr int NP = BLK / RPP;                   // passes over the block's rows
     constexpr int TOT = MODE == kFull ? 2 * NP : NP;   // K passes, then V passes (or one of them)
-    constexpr int DIST = TOT < 8 ? TOT : 8;         // loads in flight per lane
+    constexpr int RING = ES == 1 ? 4 : 8;           // loads in flight per lane (fp8: see above)
+    constexpr int DIST = TOT < RING ? TOT : RING;
     __shared__ float ps[kSplit][BLK];               // scores, then P, of each wave's block
     __shared__ float ml[kSplit][2];
     __shared__ float os[kSplit][D];
