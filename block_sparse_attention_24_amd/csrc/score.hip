@@ -357,7 +357,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     // bytes into one of two LDS stages.  Thread t moves 4-dim groups
     // t + 256 u (u = 0..3) of each operand: row (t + 256 u) / 8, group t % 8.
     // The 16-byte chunk c of row x sits at position c ^ ((x >> 2) & 3), so
-    // the MFMA reads (16 rows, one chunk each) fall in distinct banks.
+    // an MFMA read (16 consecutive rows, one chunk each) covers 16 different
+    // 16-byte bank slots of a 256-byte line instead of 4.
     constexpr int CH = 32, NC = D / CH, PLANE = 128 * CH * 2, STAGE = 4 * PLANE;
     __shared__ __attribute__((aligned(16))) char st[2 * STAGE];
     const float *qsrc[4], *ksrc[4];
