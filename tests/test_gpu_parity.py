@@ -395,6 +395,44 @@ def _sampled_check(w, inp, out, rows_per_head=12, heads=4, seed=0, gen_device=DE
           f"max O error / row magnitude {max(errs):.4f} (bar {TOL_O[w.dtype]})", flush=True)
 
 
+# Inputs with a strong common direction (the sink recipe): the block-mean
+# products are far from zero, where the score GEMM's split of each fp32
+# operand into bf16 hi + lo matters most.
+SCORE_SPLIT = [
+    wl.Workload("bf16-sink12-score", 1, 128 * 48, 8, 2, 128, 128, "bf16", sink_logit=12.0),
+    wl.Workload("fp8-sink12-score-paged", 1, 128 * 40, 8, 1, 128, 128, "fp8", paged=True, page_size=64,
+                sink_logit=12.0),
+    wl.Workload("f32-sink12-score-d64", 2, 128 * 20, 4, 2, 64, 128, "f32", sink_logit=12.0),
+]
+
+
+@pytest.mark.parametrize("w", SCORE_SPLIT, ids=lambda w: w.name)
+def test_score_split_precision(w):
+    """The score GEMM sums lo*hi + hi*lo + hi*hi of bf16 halves of the fp32
+    block means: each product lies within about 3 * 2^-18 of |qbar_i kbar_i|,
+    so a score lies within 1.2e-5 * sum_i |tau qbar_i kbar_i| of its exact
+    value, plus fp32 rounding of the sum and the value term.  Checked against
+    the fp64 oracle element by element on and below the diagonal."""
+    _announce(f"score split precision {w.name}")
+    inp = wl.make_inputs(w, device=DEV)
+    out = run_path(w, inp)
+    q, k, v = oracle_qkv(inp)
+    nb = w.num_blocks
+    s_ref = oracle.oam_scores(q, k, v, w.block)
+    qbar, kbar, _ = oracle.pool_blocks(q, k, v, w.block)
+    tau = 1.0 / math.sqrt(w.head_dim)
+    group = w.hq // w.hkv
+    absdot = np.stack([np.stack([tau * (np.abs(qbar[b, h]) @ np.abs(kbar[b, h // group]).T) for h in range(w.hq)])
+                       for b in range(w.batch)])
+    bound = 1.2e-5 * absdot + 2e-6 * np.maximum(1.0, np.abs(np.nan_to_num(s_ref, neginf=0.0)))
+    s_gpu = out["scores"].cpu().double().numpy()
+    low = np.tril(np.ones((nb, nb), dtype=bool))
+    err = np.abs(s_gpu[..., low] - s_ref[..., low])
+    print(f"  max |ds| {err.max():.3g}, max sum|tau q k| {absdot[..., low].max():.3g}", flush=True)
+    assert np.all(err <= bound[..., low])
+    assert err.max() < TOL_SCORE
+
+
 @pytest.mark.parametrize("w", [wl.GQA_8K], ids=lambda w: w.name)
 def test_full_8k_whole_oracle(w):
     _announce(f"full {w.name}")
